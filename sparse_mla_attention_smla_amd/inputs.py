@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the sparse-MLA backward workloads.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic.  Both the HIP path's tests/benchmark and the CPU oracle's
+tests take their inputs from here, so the two sides see identical bytes.
+
+Workloads follow the shapes of the DSv4 sparse-MLA training backward described
+in ROCm/aiter PR 4766 "Sparse MLA training backward" (Contract and Performance
+sections): one shared 512-wide kv tensor, per-query top-k row indices with -1
+padding, an optional per-head sink, and a "sliding window of 128 + compressed
+pool" index structure for the large cases.  The pages do not give the pool
+stride or pool selection rule; the recipe below fixes them (window 128, pool row
+j summarises tokens 4j..4j+3 and becomes eligible once 4j+3 <= t, up to 384
+uniform or Zipf(1.1) picks).
+
+Recipe (all draws from ``np.random.default_rng(1000 + workload.index)``, in the
+order indices, q, kv, dO, sink):
+
+* indices -- per row, sampled without replacement with the Efraimidis-Spirakis
+  A-ES method (key = ln(u)/w, keep the largest keys); equal weights give
+  uniform sampling.  Valid indices are stored ascending, then -1 padding.
+* q, kv, dO -- float32 standard normal, rounded to bfloat16 (round to nearest
+  even) and returned as uint16 bit patterns.
+* sink -- float32 standard normal, one value per head (always drawn, so the
+  with-sink and without-sink runs of one workload share every other tensor).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+D = 512  # fixed head dimension of the op
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int          # seed = 1000 + index
+    T: int              # query tokens
+    H: int              # heads
+    num_kv: int         # kv rows (token rows 0..T-1, then pool rows)
+    topk: int           # index slots per query token
+    selection: str      # "causal" | "swa_pool" | "swa_pool_zipf"
+    window: int = 0     # sliding-window length (swa_pool*)
+    pool_stride: int = 0
+    pool_picks: int = 0
+    zipf_s: float = 1.1
+
+    @property
+    def pool_rows(self) -> int:
+        return self.num_kv - self.T
+
+    def flops(self) -> float:
+        """Nominal backward flop count, 10*T*H*topk*512 (padded slots counted)."""
+        return 10.0 * self.T * self.H * self.topk * D
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 0, T=64, H=16, num_kv=64, topk=16, selection="causal"),
+    "small": Workload("small", 1, T=1024, H=64, num_kv=1024, topk=128, selection="causal"),
+    "headline": Workload("headline", 2, T=4096, H=128, num_kv=5120, topk=512,
+                         selection="swa_pool", window=128, pool_stride=4, pool_picks=384),
+    "skewed": Workload("skewed", 3, T=4096, H=128, num_kv=5120, topk=512,
+                       selection="swa_pool_zipf", window=128, pool_stride=4, pool_picks=384),
+    "long": Workload("long", 4, T=8192, H=128, num_kv=10240, topk=512,
+                     selection="swa_pool", window=128, pool_stride=4, pool_picks=384),
+}
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits.
+
+    Inputs here are finite normal draws, so no NaN/Inf handling is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def _aes_pick(rng: np.random.Generator, weights: np.ndarray | None, n: int, m: int) -> np.ndarray:
+    """Pick m of n items without replacement (A-ES keys ln(u)/w, largest m)."""
+    if m <= 0:
+        return np.zeros(0, dtype=np.int64)
+    u = rng.random(n)
+    if m >= n:
+        return np.arange(n, dtype=np.int64)
+    with np.errstate(divide="ignore"):
+        keys = np.log(u)
+    if weights is not None:
+        keys = keys / weights
+    part = np.argpartition(-keys, m - 1)[:m]
+    return np.sort(part)
+
+
+def make_indices(w: Workload, rng: np.random.Generator) -> np.ndarray:
+    T, K = w.T, w.topk
+    idx = np.full((T, K), -1, dtype=np.int32)
+    if w.selection == "causal":
+        for t in range(T):
+            rows = _aes_pick(rng, None, t + 1, min(K, t + 1))
+            idx[t, : rows.size] = rows
+        return idx
+    zipf = w.selection == "swa_pool_zipf"
+    P = w.pool_rows
+    zw = (np.arange(1, P + 1, dtype=np.float64)) ** (-w.zipf_s) if zipf else None
+    for t in range(T):
+        lo = max(0, t - w.window + 1)
+        win = np.arange(lo, t + 1, dtype=np.int64)
+        # pool row j is eligible once the tokens it summarises are all visible
+        n_elig = 0 if t < w.pool_stride - 1 else min(P, (t - (w.pool_stride - 1)) // w.pool_stride + 1)
+        picks = _aes_pick(rng, None if zw is None else zw[:n_elig], n_elig, min(w.pool_picks, n_elig))
+        row = np.concatenate([win, T + picks])
+        idx[t, : row.size] = row
+    return idx
+
+
+def make(name_or_workload, sink: bool = True) -> dict:
+    """Build the seeded inputs of one workload.
+
+    Returns a dict with numpy arrays: q/kv/dO (uint16 bf16 bits, [T,H,512] /
+    [num_kv,512] / [T,H,512]), idx (int32 [T,topk]), sink (float32 [H] or None),
+    and the Workload under "workload".
+    """
+    w = WORKLOADS[name_or_workload] if isinstance(name_or_workload, str) else name_or_workload
+    rng = np.random.default_rng(1000 + w.index)
+    idx = make_indices(w, rng)
+    q = f32_to_bf16_bits(rng.standard_normal((w.T, w.H, D), dtype=np.float32))
+    kv = f32_to_bf16_bits(rng.standard_normal((w.num_kv, D), dtype=np.float32))
+    dO = f32_to_bf16_bits(rng.standard_normal((w.T, w.H, D), dtype=np.float32))
+    s = rng.standard_normal(w.H).astype(np.float32)
+    return {"workload": w, "q": q, "kv": kv, "dO": dO, "idx": idx, "sink": s if sink else None}
+
+
+def shuffle_slots(idx: np.ndarray, seed: int) -> np.ndarray:
+    """Return a copy of idx with every row's slots permuted (valid and -1 mixed)."""
+    rng = np.random.default_rng(seed)
+    out = idx.copy()
+    for t in range(out.shape[0]):
+        out[t] = out[t, rng.permutation(out.shape[1])]
+    return out
