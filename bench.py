@@ -1,0 +1,272 @@
+"""Benchmark of the sparse MLA training backward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload headline]
+
+A step is one smla_bwd call (CSR build, delta, dQ, dKV-intermediate, gather,
+d_sink) over the resident, seeded headline workload (T=4096, H=128, topk=512,
+D=512, num_kv=5120: 128-row sliding window + up to 384 of 1024 pool rows).
+O and lse are produced once by the library's own forward (smla_fwd).  The
+workspace and outputs are preallocated, so nothing is allocated while timing.
+
+Prints ONE JSON line: value = nominal TFLOPS (10*T*H*topk*512 flops per call,
+padded slots counted), ms_per_step, the roofline of the dominant kernel
+(timed live with HIP events on the library's stream) and, on rank 0 at N=1,
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+D = 512
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--stage-steps", type=int, default=10)
+    return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources: a stored HBM-traffic figure is only valid for these."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_mla_attention_smla_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p))
+    except ValueError:
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(w, n_tokens):
+    """Time the fp64 oracle backward (as it stands) on an evenly spaced token sample."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import smla_oracle as orc
+    from sparse_mla_attention_smla_amd import inputs
+
+    x = inputs.make(w.name, sink=True)
+    toks = np.linspace(0, w.T - 1, n_tokens).round().astype(int)
+    scale = 1.0 / math.sqrt(D)
+    kv64 = orc.bf16_to_f64(x["kv"])
+    # O and lse of the sampled tokens from the oracle forward (not timed)
+    O = np.zeros((w.T, w.H, D), dtype=np.uint16)
+    lse = np.zeros((w.T, w.H), dtype=np.float32)
+    for t in toks:
+        o_t, l_t = orc.forward_token(orc.bf16_to_f64(x["q"][t]), kv64, x["idx"][t],
+                                     x["sink"].astype(np.float64), scale)
+        O[t], lse[t] = orc.emit_forward_outputs(o_t, l_t)
+    t0 = time.perf_counter()
+    orc.backward_tokens(x["q"], x["kv"], x["dO"], O, lse, x["idx"], x["sink"], scale, toks)
+    dt = time.perf_counter() - t0
+    flops = 10.0 * n_tokens * w.H * w.topk * D
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+        "sample": f"fp64 NumPy oracle backward (dq, P, dS, interm) on {n_tokens} evenly spaced of "
+                  f"{w.T} tokens of the {w.name} workload; {dt:.2f} s; extrapolated "
+                  f"{dt * w.T / n_tokens * 1e3:.0f} ms per full call",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no "
+              "multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_smla_amd import binding as B
+    from sparse_mla_attention_smla_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    w = inputs.WORKLOADS[args.workload]
+    T, H, N, K = w.T, w.H, w.num_kv, w.topk
+    scale = 1.0 / math.sqrt(D)
+    print(f"[bench] generating {w.name}: T={T} H={H} num_kv={N} topk={K}", file=sys.stderr, flush=True)
+    x = inputs.make(w.name, sink=True)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    q, kv, dO = d16(x["q"]), d16(x["kv"]), d16(x["dO"])
+    idx = torch.from_numpy(x["idx"]).cuda()
+    sink = torch.from_numpy(x["sink"]).cuda()
+    nnz = int((x["idx"] >= 0).sum())
+    del x
+    O, lse = B.smla_fwd(q, kv, idx, sink, scale)
+    dq = torch.empty_like(q)
+    dkv = torch.empty_like(kv)
+    d_sink = torch.empty(H, dtype=torch.float32, device="cuda")
+    ws = B.bwd_workspace(T, H, N, K, q.device)
+    torch.cuda.synchronize()
+
+    def step():
+        B.smla_bwd(q, kv, dO, O, lse, idx, sink, scale, workspace=ws, out=(dq, dkv, d_sink))
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps between synchronisations
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(args.steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)])
+    ms = float(ev[0].elapsed_time(ev[-1]) / args.steps)
+    flops = w.flops()
+    tflops = flops / (ms * 1e-3) / 1e12
+    print(f"[bench] {ms:.3f} ms/call, {tflops:.1f} TFLOPS (wall {wall * 1e3 / args.steps:.3f} ms)",
+          file=sys.stderr, flush=True)
+
+    # ---- per-stage timing (each stage entry point alone, same stream, same buffers)
+    delta = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    dsp = torch.empty((T, K, 2 * H), dtype=torch.bfloat16, device="cuda")
+    interm = torch.empty((T * K, D), dtype=torch.bfloat16, device="cuda")
+    row_ptr = torch.empty(N + 1, dtype=torch.int32, device="cuda")
+    slots = torch.empty(T * K, dtype=torch.int32, device="cuda")
+    dq2 = torch.empty_like(q)
+    dkv2 = torch.empty_like(kv)
+    ds2 = torch.empty(H, dtype=torch.float32, device="cuda")
+    csr_ws = torch.empty(B.lib().smla_csr_workspace_bytes(T, K, N), dtype=torch.uint8, device="cuda")
+    g_ws = torch.empty(B.lib().smla_gather_workspace_bytes(T, K, N), dtype=torch.uint8, device="cuda")
+    s_ws = torch.empty(max(4, B.lib().smla_dsink_workspace_bytes(T, H)), dtype=torch.uint8, device="cuda")
+    stages = {
+        "csr": lambda: B.smla_build_csr(idx, N, out=(row_ptr, slots), workspace=csr_ws),
+        "delta": lambda: B.smla_delta(O, dO, delta=delta),
+        "dq": lambda: B.smla_dq(q, kv, dO, lse, delta, idx, scale, dsp=dsp, dq=dq2),
+        "interm": lambda: B.smla_interm(q, dO, dsp, idx, N, interm=interm),
+        "gather": lambda: B.smla_gather(interm, row_ptr, slots, T, K, N, dkv=dkv2, workspace=g_ws),
+        "dsink": lambda: B.smla_dsink(lse, delta, sink, d_sink=ds2, workspace=s_ws),
+    }
+    stage_ms = {}
+    for name, fn in stages.items():
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.stage_steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        stage_ms[name] = a.elapsed_time(b) / args.stage_steps
+
+    # algorithmic work per launch (nominal: all T*topk slots), see the design notes
+    qb = T * H * D * 2
+    algo = {
+        "delta": ("hbm", 2 * qb + T * H * 4),
+        "dq": ("mfma", 6.0 * T * H * K * D),
+        "interm": ("hbm", 2 * qb + T * K * 2 * H * 2 + T * K * D * 2),
+        "gather": ("hbm", nnz * D * 2 + nnz * 4 + N * D * 2),
+    }
+    stage_rows = {}
+    for name, tms in stage_ms.items():
+        row = {"ms": round(tms, 4)}
+        if name in algo:
+            bound, work = algo[name]
+            if bound == "mfma":
+                a_ = work / (tms * 1e-3) / 1e12
+                row.update(bound="mfma", achieved_tflops=round(a_, 1), frac=round(a_ / PEAK_BF16_TFLOPS, 4))
+            else:
+                a_ = work / (tms * 1e-3) / 1e9
+                row.update(bound="hbm", achieved_gbs=round(a_, 1), frac=round(a_ / PEAK_HBM_GBS, 4))
+        stage_rows[name] = row
+    dom = max(algo, key=lambda n: stage_ms[n])
+    bound, work = algo[dom]
+    tms = stage_ms[dom]
+    if bound == "mfma":
+        achieved, peak, unit = work / (tms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / (tms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 4), "traffic": stored_traffic(dom),
+                "algorithmic_per_launch": work, "ms_per_launch": round(tms, 4)}
+
+    cpu = None
+    if args.cpu_baseline == "on":
+        print(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr,
+              flush=True)
+        cpu = cpu_baseline(w, args.cpu_sample_tokens)
+
+    out = {
+        "metric": "sparse-MLA bwd TFLOPS & ms/call at T=4096 H=128 topk=512 D=512 (1 GPU)",
+        "value": round(tflops, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "ms_median": round(float(np.median(per)), 4),
+        "ms_p10": round(float(np.percentile(per, 10)), 4),
+        "ms_p90": round(float(np.percentile(per, 90)), 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "dtype": "bf16",
+        "data": "synthetic (seeded; O and lse from the library forward)",
+        "config": {"workload": f"{w.name}: T={T} H={H} D={D} num_kv={N} topk={K}, "
+                               "SWA(128) + up to 384 of the pool rows (stride 4), sink on",
+                   "global_batch": T, "seq_len": T, "parallelism": "none (1 GPU)",
+                   "valid_slots": nnz},
+        "stages": stage_rows,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "context": {"pages_own_backward_mi355x": {"ms": 3.238, "tflops": 424},
+                    "ratio_to_pages": round(tflops / 424.0, 3),
+                    "note": "the page's pool size and selection are unknown, so its workload is "
+                            "not identical; hence vs_baseline is null"},
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

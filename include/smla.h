@@ -1,0 +1,199 @@
+/*
+ * smla.h -- C ABI of the MI355X (gfx950) sparse MLA attention library.
+ *
+ * The op is the DeepSeek-V4 sparse MLA attention of ROCm/aiter PR 4766
+ * ("[DSV4] Sparse MLA training backward"), Contract section: every query head
+ * of token t attends to its own top-k rows of ONE shared kv tensor of width
+ * 512 (K == V == kv), index -1 means "masked", the logits are scaled by
+ * `scale` (1/sqrt(512) in the page), and an optional per-head attention sink
+ * enters only the softmax denominator.  The forward's lse includes the sink.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor arguments are DEVICE pointers to caller-owned, contiguous,
+ *    row-major memory on the current HIP device.  bf16 tensors are passed as
+ *    uint16_t bit patterns.  Nothing is allocated by the library; nothing is
+ *    freed.  Inputs are read only; outputs are fully overwritten (never
+ *    accumulated into).
+ *  - D (head dimension) is fixed at 512.  Shapes: T query tokens, H heads,
+ *    num_kv kv rows, topk index slots per token.  Limits (else SMLA_ERR_SHAPE):
+ *    T >= 0, 16 <= H <= 128 with H % 16 == 0, topk >= 1, T*topk < 2^31,
+ *    num_kv >= max(T, 1) (the Contract section allows num_kv > T: rows past T
+ *    are a compressed pool) and num_kv < 2^20.
+ *  - Index values outside [0, num_kv) are masked like -1 (never read); values
+ *    other than -1 are counted into *n_invalid when that pointer is given.
+ *  - 16-byte alignment is required for bf16 tensors and the workspace, 4-byte
+ *    for float/int32 tensors (else SMLA_ERR_ALIGN).  Output and workspace
+ *    ranges must not overlap any other argument (else SMLA_ERR_INVALID_ARG).
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
+ *    work: they return without synchronising; results are ready when the
+ *    stream reaches that point.  No hipMemset is enqueued (every output cell is
+ *    written by a kernel), so calls may be captured into a HIP graph.
+ *  - Argument errors are reported synchronously before anything is enqueued.
+ *    SMLA_ERR_ARCH is returned when the current device is not gfx950 (the
+ *    page's wrapper likewise refuses other architectures).  A failed launch
+ *    returns SMLA_ERR_HIP.  The library never prints, aborts or exits.
+ *  - Results are bitwise deterministic run to run: no atomics anywhere, every
+ *    reduction has a fixed order.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SMLA_OK = 0,
+    SMLA_ERR_INVALID_ARG = 1, /* null pointer, overlap, non-finite scale, sink/d_sink mismatch */
+    SMLA_ERR_SHAPE = 2,       /* a size outside the limits above */
+    SMLA_ERR_ALIGN = 3,       /* a pointer not aligned as required */
+    SMLA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query function says */
+    SMLA_ERR_ARCH = 5,        /* current device is not gfx950 */
+    SMLA_ERR_HIP = 6          /* a HIP call or kernel launch failed */
+} smla_status;
+
+#define SMLA_D 512
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* smla_status_string(int status);
+
+/* ------------------------------------------------------------------------ */
+/* Forward (produces the backward's O and lse)                              */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * smla_fwd -- sparse MLA forward with a sink-inclusive lse.
+ * Page: aiter PR 4766, Contract section (the op; the forward's lse folds the
+ * sink into the running max and sum, lse = max + ln(sum)).
+ *   q    bf16 [T, H, 512]      kv   bf16 [num_kv, 512]
+ *   idx  int32 [T, topk]       sink float [H] or NULL (no sink)
+ *   o    bf16 [T, H, 512] out  lse  float [T, H] out
+ * For each (t, h): S_k = scale * <q[t,h], kv[idx[t,k]]> over valid slots,
+ * lse = ln(sum_k exp(S_k) + exp(sink[h])), o = sum_k exp(S_k - lse) kv[idx[t,k]].
+ * A row with no valid slot gets o = 0 and lse = -inf (no sink) or sink[h].
+ */
+int smla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
+             int T, int H, int num_kv, int topk, float scale,
+             uint16_t* o, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Backward                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of workspace smla_bwd needs for this shape (0 on a shape error). */
+size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk);
+
+/*
+ * smla_bwd -- training backward: (dq, dkv, d_sink) from (q, kv, dO, O, lse, idx, sink).
+ * Page: aiter PR 4766, Contract section (op and lse convention) and Structure
+ * table (phases delta, dQ, dKV-interm, CSR build, dKV gather, d_sink).
+ *   q, dO, o  bf16 [T, H, 512]   kv bf16 [num_kv, 512]   lse float [T, H]
+ *   idx int32 [T, topk]          sink float [H] or NULL
+ *   dq  bf16 [T, H, 512] out     dkv bf16 [num_kv, 512] out
+ *   d_sink float [H] out; must be non-NULL exactly when sink is non-NULL
+ *   n_invalid int32 [1] out or NULL: count of index values that are neither
+ *             -1 nor in [0, num_kv)
+ *   workspace device scratch of at least smla_bwd_workspace_bytes() bytes,
+ *             owned by the caller; its contents on entry do not matter.
+ * Math (per token t, head h, valid slot k): P = exp(scale*<q,kv_k> - lse),
+ * dP = <dO, kv_k>, delta = <O, dO>, dS = P*(dP - delta);
+ * dq = scale * sum_k dS kv_k;  dkv[j] = sum over slots (t,k) with idx = j of
+ * sum_h (scale*dS q[t,h] + P dO[t,h]);  d_sink[h] = -sum_t exp(sink - lse)*delta.
+ * Rows with lse = -inf contribute nothing.  dq/dkv accumulate in fp32.
+ */
+int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+             const float* lse, const int32_t* idx, const float* sink,
+             int T, int H, int num_kv, int topk, float scale,
+             uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* The backward's stages, exported individually (same conventions)          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * smla_delta -- delta[t,h] = sum_d O[t,h,d] * dO[t,h,d] (bf16 in, fp32 accumulation).
+ * Page: aiter PR 4766, Structure table, "delta = rowsum(O*dO)" row.
+ *   o, dO bf16 [T, H, 512]   delta float [T, H] out
+ */
+int smla_delta(const uint16_t* o, const uint16_t* dO, int T, int H, float* delta, void* stream);
+
+/*
+ * smla_dq -- dq and the per-slot probabilities/gradients of the logits.
+ * Page: aiter PR 4766, Structure table, "dQ" row (one LDS copy of the gathered
+ * kv feeds both the S and dP products; the kernel also emits dS and P).
+ *   q, dO bf16 [T,H,512]  kv bf16 [num_kv,512]  lse, delta float [T,H]  idx int32 [T,topk]
+ *   dq  bf16 [T, H, 512] out
+ *   dsp bf16 [T, topk, 2H] out: dsp[t,k,h] = scale*dS[t,h,k], dsp[t,k,H+h] = P[t,h,k].
+ *       Masked slots hold 0 when the 32-slot tile containing them has a valid
+ *       slot; tiles with no valid slot are left unwritten.
+ */
+int smla_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const float* lse,
+            const float* delta, const int32_t* idx, int T, int H, int num_kv, int topk,
+            float scale, uint16_t* dq, uint16_t* dsp, void* stream);
+
+/*
+ * smla_interm -- per-slot dKV intermediate, contracted over all heads.
+ * Page: aiter PR 4766, Structure table, "dKV-interm" row, and the R_CHUNK note
+ * (the intermediate is [T, topk, 512] bf16).
+ *   q, dO bf16 [T,H,512]  dsp bf16 [T,topk,2H] (from smla_dq)  idx int32 [T,topk]
+ *   interm bf16 [T*topk, 512] out: interm[t*topk+k] = sum_h dsp[t,k,h] q[t,h] + dsp[t,k,H+h] dO[t,h]
+ *       Rows of tiles with no valid slot are left unwritten; the gather never reads them.
+ */
+int smla_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* dsp, const int32_t* idx,
+                int T, int H, int num_kv, int topk, uint16_t* interm, void* stream);
+
+/* Bytes of workspace smla_build_csr needs (0 on a shape error). */
+size_t smla_csr_workspace_bytes(int T, int topk, int num_kv);
+
+/*
+ * smla_build_csr -- inverted top-k index, built on the device without atomics.
+ * Page: aiter PR 4766, Structure table, "CSR build" row (the top-k scatter is
+ * inverted so each kv row can gather its contributors).
+ *   idx int32 [T, topk]
+ *   row_ptr int32 [num_kv+1] out: row_ptr[0] = 0, row_ptr[j+1]-row_ptr[j] = number
+ *           of valid slots addressing row j
+ *   slots   int32 [T*topk] out (capacity): slots[row_ptr[j] .. row_ptr[j+1]) are the
+ *           slots s = t*topk + k with idx[t,k] == j, strictly increasing; entries
+ *           past row_ptr[num_kv] are left unwritten
+ *   n_invalid int32 [1] out or NULL
+ */
+int smla_build_csr(const int32_t* idx, int T, int topk, int num_kv,
+                   int32_t* row_ptr, int32_t* slots, int32_t* n_invalid,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace smla_gather needs (0 on a shape error). */
+size_t smla_gather_workspace_bytes(int T, int topk, int num_kv);
+
+/*
+ * smla_gather -- dkv[j] = bf16( sum over s in slots[row_ptr[j]..row_ptr[j+1]) of interm[s] ),
+ * fp32 accumulation in a fixed order; rows with no contributor get 0.
+ * Page: aiter PR 4766, Structure table, "dKV gather" row (atomic-free: each kv
+ * row gathers its own contributors).
+ *   interm bf16 [T*topk, 512]  row_ptr int32 [num_kv+1]  slots int32 [row_ptr[num_kv]]
+ *   dkv bf16 [num_kv, 512] out
+ */
+int smla_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots,
+                int T, int topk, int num_kv, uint16_t* dkv,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace smla_dsink needs (0 on a shape error). */
+size_t smla_dsink_workspace_bytes(int T, int H);
+
+/*
+ * smla_dsink -- d_sink[h] = -sum_t exp(sink[h] - lse[t,h]) * delta[t,h] (fixed-order sum).
+ * Page: aiter PR 4766, Structure table, "d_sink" row.  The formula is the
+ * derivative of O with respect to the sink logit: dO/dsink = -P_sink * O.
+ *   lse, delta float [T, H]  sink float [H]  d_sink float [H] out
+ */
+int smla_dsink(const float* lse, const float* delta, const float* sink, int T, int H,
+               float* d_sink, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

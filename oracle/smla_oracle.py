@@ -287,6 +287,18 @@ def delta(dO, O):
     return np.stack([np.sum(_as64(O[t]) * _as64(dO[t]), axis=1) for t in range(T)])
 
 
+def dkv_from_interm(interm, idx, num_kv):
+    """dkv[j] = sum of interm[t, k] over valid slots (t, k) with idx[t, k] == j
+    (the gather phase).  interm: [T, K, D] (bf16 bits or floats)."""
+    it = _as64(interm)
+    T, K, Dh = it.shape
+    flat = np.asarray(idx, dtype=np.int64).reshape(-1)
+    v = (flat >= 0) & (flat < num_kv)
+    dkv = np.zeros((num_kv, Dh))
+    np.add.at(dkv, flat[v], it.reshape(T * K, Dh)[v])
+    return dkv
+
+
 # --------------------------------------------------------------------------
 # inverted top-k (CSR)
 # --------------------------------------------------------------------------

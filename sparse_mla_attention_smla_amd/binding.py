@@ -1,0 +1,272 @@
+"""Thin ctypes binding of libsmla.so (the C ABI in include/smla.h).
+
+Argument marshalling only: torch tensors -> device pointers, the current HIP
+stream -> a stream handle, C status codes -> exceptions.  Every computation runs
+in the library's HIP kernels; there is no fallback path.  If the library is
+missing, every call raises.
+
+Function names follow the C entry points: smla_fwd, smla_bwd, smla_delta,
+smla_dq, smla_interm, smla_build_csr, smla_gather, smla_dsink.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+D = 512
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsmla.so")
+
+_lib = None
+_lib_lock = threading.Lock()
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_Z = ctypes.c_size_t
+
+_SIGNATURES = {
+    "smla_status_string": ([_I], ctypes.c_char_p),
+    "smla_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "smla_bwd_workspace_bytes": ([_I, _I, _I, _I], _Z),
+    "smla_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "smla_delta": ([_P, _P, _I, _I, _P, _P], _I),
+    "smla_dq": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "smla_interm": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "smla_csr_workspace_bytes": ([_I, _I, _I], _Z),
+    "smla_build_csr": ([_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
+    "smla_gather_workspace_bytes": ([_I, _I, _I], _Z),
+    "smla_gather": ([_P, _P, _P, _I, _I, _I, _P, _P, _Z, _P], _I),
+    "smla_dsink_workspace_bytes": ([_I, _I], _Z),
+    "smla_dsink": ([_P, _P, _P, _I, _I, _P, _P, _Z, _P], _I),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+
+
+def lib():
+    """Load libsmla.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lib_lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise RuntimeError(
+                        f"{LIB_PATH} is missing: build it with "
+                        "`python -m sparse_mla_attention_smla_amd.build`")
+                h = ctypes.CDLL(LIB_PATH)
+                for name, (args, res) in _SIGNATURES.items():
+                    f = getattr(h, name)
+                    f.argtypes = args
+                    f.restype = res
+                _lib = h
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().smla_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise SmlaError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _default_scale(scale):
+    return 1.0 / math.sqrt(D) if scale is None else float(scale)
+
+
+# ---------------------------------------------------------------------------
+# forward / backward
+# ---------------------------------------------------------------------------
+
+def smla_fwd(q, kv, idx, sink=None, scale=None):
+    """Sparse MLA forward: (o bf16 [T,H,512], lse fp32 [T,H]).  lse includes the sink."""
+    T, H, _ = q.shape
+    N, K = kv.shape[0], idx.shape[1]
+    _need(q, "q", torch.bfloat16, (T, H, D))
+    _need(kv, "kv", torch.bfloat16, (N, D))
+    _need(idx, "idx", torch.int32, (T, K))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (H,))
+    o = torch.empty_like(q)
+    lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    _check("smla_fwd", lib().smla_fwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(sink), T, H, N, K,
+                                      _default_scale(scale), _ptr(o), _ptr(lse), _stream(q.device)))
+    return o, lse
+
+
+def bwd_workspace_bytes(T, H, num_kv, topk) -> int:
+    n = lib().smla_bwd_workspace_bytes(T, H, num_kv, topk)
+    if n == 0:
+        raise SmlaError("smla_bwd_workspace_bytes", 2)
+    return n
+
+
+_ws_cache: dict = {}
+
+
+def bwd_workspace(T, H, num_kv, topk, device):
+    """A cached workspace buffer for this shape and device."""
+    key = (T, H, num_kv, topk, str(device))
+    ws = _ws_cache.get(key)
+    if ws is None:
+        ws = torch.empty(bwd_workspace_bytes(T, H, num_kv, topk), dtype=torch.uint8, device=device)
+        _ws_cache[key] = ws
+    return ws
+
+
+def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=None,
+             count_invalid=False):
+    """Sparse MLA backward: returns (dq, dkv, d_sink[, n_invalid]).
+
+    out, if given, is a tuple (dq, dkv, d_sink) of preallocated outputs.
+    """
+    T, H, _ = q.shape
+    N, K = kv.shape[0], idx.shape[1]
+    _need(q, "q", torch.bfloat16, (T, H, D))
+    _need(kv, "kv", torch.bfloat16, (N, D))
+    _need(dO, "dO", torch.bfloat16, (T, H, D))
+    _need(o, "o", torch.bfloat16, (T, H, D))
+    _need(lse, "lse", torch.float32, (T, H))
+    _need(idx, "idx", torch.int32, (T, K))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (H,))
+    if out is None:
+        dq = torch.empty_like(q)
+        dkv = torch.empty_like(kv)
+        d_sink = torch.empty((H,), dtype=torch.float32, device=q.device) if sink is not None else None
+    else:
+        dq, dkv, d_sink = out
+    if workspace is None:
+        workspace = bwd_workspace(T, H, N, K, q.device)
+    n_inv = torch.empty((1,), dtype=torch.int32, device=q.device) if count_invalid else None
+    _check("smla_bwd", lib().smla_bwd(
+        _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), T, H, N, K,
+        _default_scale(scale), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
+        _ptr(workspace), workspace.numel(), _stream(q.device)))
+    if count_invalid:
+        return dq, dkv, d_sink, n_inv
+    return dq, dkv, d_sink
+
+
+# ---------------------------------------------------------------------------
+# stages
+# ---------------------------------------------------------------------------
+
+def smla_delta(o, dO, delta=None):
+    T, H, _ = o.shape
+    _need(o, "o", torch.bfloat16, (T, H, D))
+    _need(dO, "dO", torch.bfloat16, (T, H, D))
+    if delta is None:
+        delta = torch.empty((T, H), dtype=torch.float32, device=o.device)
+    _check("smla_delta", lib().smla_delta(_ptr(o), _ptr(dO), T, H, _ptr(delta), _stream(o.device)))
+    return delta
+
+
+def smla_dq(q, kv, dO, lse, delta, idx, scale=None, dsp=None, dq=None):
+    """Returns (dq bf16 [T,H,512], dsp bf16 [T,topk,2H]) with dsp = [scale*dS | P] per slot."""
+    T, H, _ = q.shape
+    N, K = kv.shape[0], idx.shape[1]
+    for t, n, dt, sh in ((q, "q", torch.bfloat16, (T, H, D)), (kv, "kv", torch.bfloat16, (N, D)),
+                         (dO, "dO", torch.bfloat16, (T, H, D)), (lse, "lse", torch.float32, (T, H)),
+                         (delta, "delta", torch.float32, (T, H)), (idx, "idx", torch.int32, (T, K))):
+        _need(t, n, dt, sh)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dsp is None:
+        dsp = torch.empty((T, K, 2 * H), dtype=torch.bfloat16, device=q.device)
+    _check("smla_dq", lib().smla_dq(_ptr(q), _ptr(kv), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(idx),
+                                    T, H, N, K, _default_scale(scale), _ptr(dq), _ptr(dsp),
+                                    _stream(q.device)))
+    return dq, dsp
+
+
+def smla_interm(q, dO, dsp, idx, num_kv, interm=None):
+    T, H, _ = q.shape
+    K = idx.shape[1]
+    _need(q, "q", torch.bfloat16, (T, H, D))
+    _need(dO, "dO", torch.bfloat16, (T, H, D))
+    _need(dsp, "dsp", torch.bfloat16, (T, K, 2 * H))
+    _need(idx, "idx", torch.int32, (T, K))
+    if interm is None:
+        interm = torch.empty((T * K, D), dtype=torch.bfloat16, device=q.device)
+    _check("smla_interm", lib().smla_interm(_ptr(q), _ptr(dO), _ptr(dsp), _ptr(idx), T, H, num_kv, K,
+                                            _ptr(interm), _stream(q.device)))
+    return interm
+
+
+def smla_build_csr(idx, num_kv, count_invalid=False, out=None, workspace=None):
+    """Returns (row_ptr int32 [num_kv+1], slots int32 [T*topk] capacity[, n_invalid])."""
+    T, K = idx.shape
+    _need(idx, "idx", torch.int32, (T, K))
+    if out is None:
+        row_ptr = torch.empty((num_kv + 1,), dtype=torch.int32, device=idx.device)
+        slots = torch.empty((max(T * K, 1),), dtype=torch.int32, device=idx.device)
+    else:
+        row_ptr, slots = out
+    n = lib().smla_csr_workspace_bytes(T, K, num_kv)
+    if n == 0:
+        raise SmlaError("smla_csr_workspace_bytes", 2)
+    ws = torch.empty((n,), dtype=torch.uint8, device=idx.device) if workspace is None else workspace
+    n_inv = torch.empty((1,), dtype=torch.int32, device=idx.device) if count_invalid else None
+    _check("smla_build_csr", lib().smla_build_csr(_ptr(idx), T, K, num_kv, _ptr(row_ptr), _ptr(slots),
+                                                  _ptr(n_inv), _ptr(ws), n, _stream(idx.device)))
+    return (row_ptr, slots, n_inv) if count_invalid else (row_ptr, slots)
+
+
+def smla_gather(interm, row_ptr, slots, T, topk, num_kv, dkv=None, workspace=None):
+    _need(interm, "interm", torch.bfloat16, (T * topk, D))
+    _need(row_ptr, "row_ptr", torch.int32, (num_kv + 1,))
+    _need(slots, "slots", torch.int32)
+    if dkv is None:
+        dkv = torch.empty((num_kv, D), dtype=torch.bfloat16, device=interm.device)
+    n = lib().smla_gather_workspace_bytes(T, topk, num_kv)
+    if n == 0:
+        raise SmlaError("smla_gather_workspace_bytes", 2)
+    ws = torch.empty((n,), dtype=torch.uint8, device=interm.device) if workspace is None else workspace
+    _check("smla_gather", lib().smla_gather(_ptr(interm), _ptr(row_ptr), _ptr(slots), T, topk, num_kv,
+                                            _ptr(dkv), _ptr(ws), n, _stream(interm.device)))
+    return dkv
+
+
+def smla_dsink(lse, delta, sink, d_sink=None, workspace=None):
+    T, H = lse.shape
+    _need(lse, "lse", torch.float32, (T, H))
+    _need(delta, "delta", torch.float32, (T, H))
+    _need(sink, "sink", torch.float32, (H,))
+    if d_sink is None:
+        d_sink = torch.empty((H,), dtype=torch.float32, device=lse.device)
+    n = lib().smla_dsink_workspace_bytes(T, H)
+    ws = torch.empty((max(n, 4),), dtype=torch.uint8, device=lse.device) if workspace is None else workspace
+    _check("smla_dsink", lib().smla_dsink(_ptr(lse), _ptr(delta), _ptr(sink), T, H, _ptr(d_sink),
+                                          _ptr(ws), n, _stream(lse.device)))
+    return d_sink

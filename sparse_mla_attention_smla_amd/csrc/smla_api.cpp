@@ -1,0 +1,338 @@
+// Host side of the C ABI declared in include/smla.h: argument validation, the
+// gfx950 gate, workspace carving and the launch order of the backward.
+//
+// Page: aiter PR 4766 "Sparse MLA training backward" -- the public wrapper of
+// the page checks head_dim == 512, kv/dO/O shapes, num_kv >= T and
+// contiguity, defaults the scale to 1/sqrt(D) and refuses non-gfx950 devices;
+// its review asks for dtype and lse/sink shape checks too.  Here the same
+// checks are made on raw sizes and pointers before anything is enqueued.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "smla.h"
+#include "smla_launch.hpp"
+#include "smla_device.hpp"
+
+using namespace smla;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+int g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::mutex g_arch_mu;
+
+smla_status check_arch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SMLA_ERR_ARCH;
+    std::lock_guard<std::mutex> lk(g_arch_mu);
+    if (g_arch_state[dev] == 0) {
+        hipDeviceProp_t prop;
+        if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SMLA_ERR_HIP;
+        g_arch_state[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return g_arch_state[dev] == 1 ? SMLA_OK : SMLA_ERR_ARCH;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+    const void* p;
+    size_t n;
+};
+
+bool overlap(Range a, Range b) {
+    if (a.p == nullptr || b.p == nullptr || a.n == 0 || b.n == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+// all[first_out..nall) are outputs: each must be disjoint from every other range
+bool outputs_disjoint(const Range* all, int nall, int first_out) {
+    for (int i = first_out; i < nall; ++i)
+        for (int j = 0; j < nall; ++j)
+            if (i != j && overlap(all[i], all[j])) return false;
+    return true;
+}
+
+smla_status check_shape(int T, int H, int num_kv, int topk) {
+    if (T < 0 || H < 16 || H > 128 || H % 16 != 0 || topk < 1) return SMLA_ERR_SHAPE;
+    if (num_kv < 1 || num_kv < T || num_kv >= (1 << 20)) return SMLA_ERR_SHAPE;
+    if ((int64_t)T * topk >= (int64_t)1 << 31) return SMLA_ERR_SHAPE;
+    return SMLA_OK;
+}
+
+smla_status hip_status(hipError_t e) { return e == hipSuccess ? SMLA_OK : SMLA_ERR_HIP; }
+
+constexpr size_t kWsAlign = 256;
+
+struct BwdLayout {
+    size_t delta, dsp, interm, row_ptr, slots, csr, gather, dsink, total;
+};
+
+BwdLayout bwd_layout(int T, int H, int num_kv, int topk) {
+    const int64_t M = (int64_t)T * topk;
+    BwdLayout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes, kWsAlign);
+        return at;
+    };
+    L.delta = take((size_t)T * H * 4);
+    L.dsp = take((size_t)M * 2 * H * 2);
+    L.interm = take((size_t)M * kD * 2);
+    L.row_ptr = take((size_t)(num_kv + 1) * 4);
+    L.slots = take((size_t)(M > 0 ? M : 1) * 4);
+    L.csr = take(csr_scratch_bytes(M, num_kv));
+    L.gather = take(gather_scratch_bytes(M, num_kv));
+    L.dsink = take((size_t)(dsink_blocks(T) > 0 ? dsink_blocks(T) : 1) * H * 4);
+    L.total = off;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* smla_status_string(int status) {
+    switch (status) {
+        case SMLA_OK: return "ok";
+        case SMLA_ERR_INVALID_ARG: return "invalid argument";
+        case SMLA_ERR_SHAPE: return "unsupported shape";
+        case SMLA_ERR_ALIGN: return "misaligned pointer";
+        case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
+        case SMLA_ERR_ARCH: return "device is not gfx950";
+        case SMLA_ERR_HIP: return "HIP error";
+        default: return "unknown status";
+    }
+}
+
+size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk) {
+    if (check_shape(T, H, num_kv, topk) != SMLA_OK) return 0;
+    return bwd_layout(T, H, num_kv, topk).total;
+}
+
+size_t smla_csr_workspace_bytes(int T, int topk, int num_kv) {
+    if (check_shape(T, 16, num_kv, topk) != SMLA_OK) return 0;
+    return csr_scratch_bytes((int64_t)T * topk, num_kv);
+}
+
+size_t smla_gather_workspace_bytes(int T, int topk, int num_kv) {
+    if (check_shape(T, 16, num_kv, topk) != SMLA_OK) return 0;
+    return gather_scratch_bytes((int64_t)T * topk, num_kv);
+}
+
+size_t smla_dsink_workspace_bytes(int T, int H) {
+    if (check_shape(T, H, T > 0 ? T : 1, 1) != SMLA_OK) return 0;
+    return (size_t)(dsink_blocks(T) > 0 ? dsink_blocks(T) : 1) * H * 4;
+}
+
+int smla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
+             int T, int H, int num_kv, int topk, float scale, uint16_t* o, float* lse,
+             void* stream) {
+    smla_status st = check_shape(T, H, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !idx || !o || !lse)) return SMLA_ERR_INVALID_ARG;
+    if (!kv) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(o, 16) || !aligned(idx, 4) ||
+        !aligned(lse, 4) || !aligned(sink, 4))
+        return SMLA_ERR_ALIGN;
+    const size_t qb = (size_t)T * H * kD * 2;
+    const Range all[] = {{q, qb}, {kv, (size_t)num_kv * kD * 2}, {idx, (size_t)T * topk * 4},
+                         {sink, sink ? (size_t)H * 4 : 0}, {o, qb}, {lse, (size_t)T * H * 4}};
+    if (!outputs_disjoint(all, 6, 4)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+    return hip_status(launch_fwd(q, kv, idx, sink, T, H, num_kv, topk, scale, o, lse,
+                                 static_cast<hipStream_t>(stream)));
+}
+
+int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+             const float* lse, const int32_t* idx, const float* sink, int T, int H, int num_kv,
+             int topk, float scale, uint16_t* dq, uint16_t* dkv, float* d_sink,
+             int32_t* n_invalid, void* workspace, size_t workspace_bytes, void* stream) {
+    smla_status st = check_shape(T, H, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+    if (!kv || !dkv) return SMLA_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !dO || !o || !lse || !idx || !dq)) return SMLA_ERR_INVALID_ARG;
+    if ((sink == nullptr) != (d_sink == nullptr)) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(dO, 16) || !aligned(o, 16) ||
+        !aligned(dq, 16) || !aligned(dkv, 16) || !aligned(lse, 4) || !aligned(idx, 4) ||
+        !aligned(sink, 4) || !aligned(d_sink, 4) || !aligned(n_invalid, 4) ||
+        !aligned(workspace, 16))
+        return SMLA_ERR_ALIGN;
+    const BwdLayout L = bwd_layout(T, H, num_kv, topk);
+    if (workspace == nullptr || workspace_bytes < L.total) return SMLA_ERR_WORKSPACE;
+    const size_t qb = (size_t)T * H * kD * 2;
+    const size_t hb = (size_t)H * 4;
+    const Range all[] = {{q, qb},
+                         {kv, (size_t)num_kv * kD * 2},
+                         {dO, qb},
+                         {o, qb},
+                         {lse, (size_t)T * H * 4},
+                         {idx, (size_t)T * topk * 4},
+                         {sink, sink ? hb : 0},
+                         {dq, qb},
+                         {dkv, (size_t)num_kv * kD * 2},
+                         {d_sink, d_sink ? hb : 0},
+                         {n_invalid, n_invalid ? 4u : 0u},
+                         {workspace, L.total}};
+    if (!outputs_disjoint(all, 12, 7)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(ws + L.delta);
+    uint16_t* dsp = reinterpret_cast<uint16_t*>(ws + L.dsp);
+    uint16_t* interm = reinterpret_cast<uint16_t*>(ws + L.interm);
+    int32_t* row_ptr = reinterpret_cast<int32_t*>(ws + L.row_ptr);
+    int32_t* slots = reinterpret_cast<int32_t*>(ws + L.slots);
+    const int64_t M = (int64_t)T * topk;
+    const CsrScratch cs = csr_carve(ws + L.csr, M, num_kv);
+    const GatherScratch gs = gather_carve(ws + L.gather, M, num_kv);
+    float* dsink_part = reinterpret_cast<float*>(ws + L.dsink);
+
+    hipError_t e;
+    // The CSR depends only on the indices; it goes first.
+    if ((e = launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, s)) != hipSuccess) return SMLA_ERR_HIP;
+    if ((e = launch_delta(o, dO, (int64_t)T * H, delta, s)) != hipSuccess) return SMLA_ERR_HIP;
+    if ((e = launch_dq(q, kv, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dsp, s)) != hipSuccess)
+        return SMLA_ERR_HIP;
+    if ((e = launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm, s)) != hipSuccess)
+        return SMLA_ERR_HIP;
+    if ((e = launch_gather(interm, row_ptr, slots, M, num_kv, gs, dkv, s)) != hipSuccess)
+        return SMLA_ERR_HIP;
+    if (sink != nullptr)
+        if ((e = launch_dsink(lse, delta, sink, T, H, dsink_part, d_sink, s)) != hipSuccess)
+            return SMLA_ERR_HIP;
+    return SMLA_OK;
+}
+
+int smla_delta(const uint16_t* o, const uint16_t* dO, int T, int H, float* delta, void* stream) {
+    smla_status st = check_shape(T, H, T > 0 ? T : 1, 1);
+    if (st != SMLA_OK) return st;
+    if (T > 0 && (!o || !dO || !delta)) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(delta, 4)) return SMLA_ERR_ALIGN;
+    const size_t qb = (size_t)T * H * kD * 2;
+    const Range all[] = {{o, qb}, {dO, qb}, {delta, (size_t)T * H * 4}};
+    if (!outputs_disjoint(all, 3, 2)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+    return hip_status(launch_delta(o, dO, (int64_t)T * H, delta, static_cast<hipStream_t>(stream)));
+}
+
+int smla_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const float* lse,
+            const float* delta, const int32_t* idx, int T, int H, int num_kv, int topk,
+            float scale, uint16_t* dq, uint16_t* dsp, void* stream) {
+    smla_status st = check_shape(T, H, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+    if (!kv || (T > 0 && (!q || !dO || !lse || !delta || !idx || !dq || !dsp)))
+        return SMLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(dO, 16) || !aligned(dq, 16) ||
+        !aligned(dsp, 16) || !aligned(lse, 4) || !aligned(delta, 4) || !aligned(idx, 4))
+        return SMLA_ERR_ALIGN;
+    const size_t qb = (size_t)T * H * kD * 2;
+    const Range all[] = {{q, qb},          {kv, (size_t)num_kv * kD * 2},
+                         {dO, qb},         {lse, (size_t)T * H * 4},
+                         {delta, (size_t)T * H * 4}, {idx, (size_t)T * topk * 4},
+                         {dq, qb},         {dsp, (size_t)T * topk * 2 * H * 2}};
+    if (!outputs_disjoint(all, 8, 6)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+    return hip_status(launch_dq(q, kv, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dsp,
+                                static_cast<hipStream_t>(stream)));
+}
+
+int smla_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* dsp, const int32_t* idx,
+                int T, int H, int num_kv, int topk, uint16_t* interm, void* stream) {
+    smla_status st = check_shape(T, H, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    if (T > 0 && (!q || !dO || !dsp || !idx || !interm)) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(dO, 16) || !aligned(dsp, 16) || !aligned(interm, 16) ||
+        !aligned(idx, 4))
+        return SMLA_ERR_ALIGN;
+    const size_t qb = (size_t)T * H * kD * 2;
+    const Range all[] = {{q, qb},
+                         {dO, qb},
+                         {dsp, (size_t)T * topk * 2 * H * 2},
+                         {idx, (size_t)T * topk * 4},
+                         {interm, (size_t)T * topk * kD * 2}};
+    if (!outputs_disjoint(all, 5, 4)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+    return hip_status(launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int smla_build_csr(const int32_t* idx, int T, int topk, int num_kv, int32_t* row_ptr,
+                   int32_t* slots, int32_t* n_invalid, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+    smla_status st = check_shape(T, 16, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    const int64_t M = (int64_t)T * topk;
+    if (!row_ptr || (M > 0 && (!idx || !slots))) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(idx, 4) || !aligned(row_ptr, 4) || !aligned(slots, 4) || !aligned(n_invalid, 4) ||
+        !aligned(workspace, 16))
+        return SMLA_ERR_ALIGN;
+    const size_t need = csr_scratch_bytes(M, num_kv);
+    if (workspace == nullptr || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
+    const Range all[] = {{idx, (size_t)M * 4},
+                         {row_ptr, (size_t)(num_kv + 1) * 4},
+                         {slots, (size_t)M * 4},
+                         {n_invalid, n_invalid ? 4u : 0u},
+                         {workspace, need}};
+    if (!outputs_disjoint(all, 5, 1)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+    return hip_status(launch_csr(idx, M, num_kv, csr_carve(workspace, M, num_kv), row_ptr, slots,
+                                 n_invalid, static_cast<hipStream_t>(stream)));
+}
+
+int smla_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots, int T,
+                int topk, int num_kv, uint16_t* dkv, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    smla_status st = check_shape(T, 16, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    const int64_t M = (int64_t)T * topk;
+    if (!row_ptr || !dkv || (M > 0 && (!interm || !slots))) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(interm, 16) || !aligned(dkv, 16) || !aligned(row_ptr, 4) || !aligned(slots, 4) ||
+        !aligned(workspace, 16))
+        return SMLA_ERR_ALIGN;
+    const size_t need = gather_scratch_bytes(M, num_kv);
+    if (workspace == nullptr || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
+    const Range all[] = {{interm, (size_t)M * kD * 2},
+                         {row_ptr, (size_t)(num_kv + 1) * 4},
+                         {slots, (size_t)M * 4},
+                         {dkv, (size_t)num_kv * kD * 2},
+                         {workspace, need}};
+    if (!outputs_disjoint(all, 5, 3)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+    return hip_status(launch_gather(interm, row_ptr, slots, M, num_kv,
+                                    gather_carve(workspace, M, num_kv), dkv,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int smla_dsink(const float* lse, const float* delta, const float* sink, int T, int H,
+               float* d_sink, void* workspace, size_t workspace_bytes, void* stream) {
+    smla_status st = check_shape(T, H, T > 0 ? T : 1, 1);
+    if (st != SMLA_OK) return st;
+    if (!sink || !d_sink || (T > 0 && (!lse || !delta))) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(lse, 4) || !aligned(delta, 4) || !aligned(sink, 4) || !aligned(d_sink, 4) ||
+        !aligned(workspace, 4))
+        return SMLA_ERR_ALIGN;
+    const size_t need = smla_dsink_workspace_bytes(T, H);
+    if (workspace == nullptr || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
+    const Range all[] = {{lse, (size_t)T * H * 4},
+                         {delta, (size_t)T * H * 4},
+                         {sink, (size_t)H * 4},
+                         {d_sink, (size_t)H * 4},
+                         {workspace, need}};
+    if (!outputs_disjoint(all, 5, 3)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+    return hip_status(launch_dsink(lse, delta, sink, T, H, static_cast<float*>(workspace), d_sink,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Device-side building blocks shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kD = 512;           // head dimension, fixed by the op
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    bf16x2 v = __builtin_convertvector(f32x2{lo, hi}, bf16x2);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// D(16x16, f32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l supplies A row (l%16) and B column (l%16), each with the 8 reduction
+// elements of group l/16; the accumulator lane l holds column l%16, rows
+// 4*(l/16) .. 4*(l/16)+3.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+// L2).  Remap so that XCD x works on the x-th contiguous eighth of the
+// logical index range: neighbouring tokens then share an L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    if ((nblocks & 7) != 0) return bid;
+    return (bid & 7) * (nblocks >> 3) + (bid >> 3);
+}
+
+__device__ __forceinline__ bool valid_row(int r, int num_kv) {
+    return (unsigned)r < (unsigned)num_kv;
+}
+
+template <typename T>
+__device__ __forceinline__ T wave_xor(T v, int mask) {
+    return __shfl_xor(v, mask, 64);
+}
+
+}  // namespace smla

@@ -1,0 +1,59 @@
+// Host-side launchers of the gfx950 kernels (one per kernel family).  Every
+// launcher only enqueues on `stream`; shapes were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace smla {
+
+// ---- streaming ------------------------------------------------------------
+hipError_t launch_delta(const uint16_t* o, const uint16_t* dO, int64_t rows, float* delta,
+                        hipStream_t s);
+constexpr int kDsinkTokensPerBlock = 32;
+inline int dsink_blocks(int T) { return (T + kDsinkTokensPerBlock - 1) / kDsinkTokensPerBlock; }
+hipError_t launch_dsink(const float* lse, const float* delta, const float* sink, int T, int H,
+                        float* partial, float* d_sink, hipStream_t s);
+
+// ---- CSR ------------------------------------------------------------------
+constexpr int kCsrBlock = 4096;  // keys per sort block (12-bit in-block position)
+inline int64_t csr_blocks(int64_t M) { return (M + kCsrBlock - 1) / kCsrBlock; }
+struct CsrScratch {
+    uint32_t* sorted;   // [M]        block-sorted packed (row << 12 | position)
+    int32_t* cnt;       // [nblk * N] per-block row counts, then per-block row offsets
+    int32_t* total;     // [N]        per-row totals
+    int32_t* inv;       // [nblk]     per-block count of out-of-range indices
+};
+size_t csr_scratch_bytes(int64_t M, int N);
+CsrScratch csr_carve(void* base, int64_t M, int N);
+hipError_t launch_csr(const int32_t* idx, int64_t M, int N, const CsrScratch& ws, int32_t* row_ptr,
+                      int32_t* slots, int32_t* n_invalid, hipStream_t s);
+
+// ---- gather ---------------------------------------------------------------
+constexpr int kGatherSeg = 128;  // contributors per gather segment
+inline int64_t gather_max_segments(int64_t M, int N) { return N + (M + kGatherSeg - 1) / kGatherSeg; }
+struct GatherScratch {
+    int32_t* seg_ptr;   // [N + 1]
+    int32_t* seg_row;   // [max segments]
+    float* partial;     // [max segments * 512]
+};
+size_t gather_scratch_bytes(int64_t M, int N);
+GatherScratch gather_carve(void* base, int64_t M, int N);
+hipError_t launch_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots,
+                         int64_t M, int N, const GatherScratch& ws, uint16_t* dkv, hipStream_t s);
+
+// ---- attention tiles (MFMA) -----------------------------------------------
+hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const float* lse,
+                     const float* delta, const int32_t* idx, int T, int H, int N, int K, float scale,
+                     uint16_t* dq, uint16_t* dsp, hipStream_t s);
+hipError_t launch_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
+                      int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
+                      hipStream_t s);
+hipError_t launch_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* dsp,
+                         const int32_t* idx, int T, int H, int N, int K, uint16_t* interm,
+                         hipStream_t s);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace smla

@@ -13,19 +13,25 @@ stride or pool selection rule; the recipe below fixes them (window 128, pool row
 j summarises tokens 4j..4j+3 and becomes eligible once 4j+3 <= t, up to 384
 uniform or Zipf(1.1) picks).
 
-Recipe (all draws from ``np.random.default_rng(1000 + workload.index)``, in the
-order indices, q, kv, dO, sink):
+Recipe (seed s = 1000 + workload.index):
 
-* indices -- per row, sampled without replacement with the Efraimidis-Spirakis
-  A-ES method (key = ln(u)/w, keep the largest keys); equal weights give
-  uniform sampling.  Valid indices are stored ascending, then -1 padding.
-* q, kv, dO -- float32 standard normal, rounded to bfloat16 (round to nearest
-  even) and returned as uint16 bit patterns.
-* sink -- float32 standard normal, one value per head (always drawn, so the
-  with-sink and without-sink runs of one workload share every other tensor).
+* indices -- from ``np.random.default_rng(s)``: per row, sampled without
+  replacement with the Efraimidis-Spirakis A-ES method (key = ln(u)/w, keep the
+  largest keys); equal weights give uniform sampling.  Valid indices are stored
+  ascending, then -1 padding.
+* sink -- next from the same generator: float32 standard normal, one value per
+  head (always drawn, so the with-sink and without-sink runs of one workload
+  share every other tensor).
+* q, kv, dO -- float32 standard normal rounded to bfloat16 (nearest, ties to
+  even), returned as uint16 bit patterns.  Each tensor is drawn in chunks of
+  2**22 values; chunk c of tensor k (q=1, kv=2, dO=3) comes from
+  ``np.random.default_rng([s, k, c])``, so chunks can be drawn in parallel
+  threads and the result does not depend on the thread count.
 """
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -115,6 +121,31 @@ def make_indices(w: Workload, rng: np.random.Generator) -> np.ndarray:
     return idx
 
 
+_CHUNK = 1 << 22
+
+
+def normal_bf16(shape, seed: int, tensor: int, threads: int | None = None) -> np.ndarray:
+    """Standard-normal float32 draws rounded to bf16 bits, chunk-seeded (see recipe)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16)
+
+    def fill(c):
+        lo = c * _CHUNK
+        hi = min(n, lo + _CHUNK)
+        x = np.random.default_rng([seed, tensor, c]).standard_normal(hi - lo, dtype=np.float32)
+        out[lo:hi] = f32_to_bf16_bits(x)
+
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    threads = threads or min(16, os.cpu_count() or 1)
+    if nchunks <= 1 or threads <= 1:
+        for c in range(nchunks):
+            fill(c)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(fill, range(nchunks)))
+    return out.reshape(shape)
+
+
 def make(name_or_workload, sink: bool = True) -> dict:
     """Build the seeded inputs of one workload.
 
@@ -123,12 +154,13 @@ def make(name_or_workload, sink: bool = True) -> dict:
     and the Workload under "workload".
     """
     w = WORKLOADS[name_or_workload] if isinstance(name_or_workload, str) else name_or_workload
-    rng = np.random.default_rng(1000 + w.index)
+    seed = 1000 + w.index
+    rng = np.random.default_rng(seed)
     idx = make_indices(w, rng)
-    q = f32_to_bf16_bits(rng.standard_normal((w.T, w.H, D), dtype=np.float32))
-    kv = f32_to_bf16_bits(rng.standard_normal((w.num_kv, D), dtype=np.float32))
-    dO = f32_to_bf16_bits(rng.standard_normal((w.T, w.H, D), dtype=np.float32))
     s = rng.standard_normal(w.H).astype(np.float32)
+    q = normal_bf16((w.T, w.H, D), seed, 1)
+    kv = normal_bf16((w.num_kv, D), seed, 2)
+    dO = normal_bf16((w.T, w.H, D), seed, 3)
     return {"workload": w, "q": q, "kv": kv, "dO": dO, "idx": idx, "sink": s if sink else None}
 
 

@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load and export every entry point include/smla.h declares,
+and argument errors must come back as status codes before any HIP call -- so
+they can be forced here with fake (never dereferenced) device addresses.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_mla_attention_smla_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "smla.h")
+
+OK, INVALID, SHAPE, ALIGN, WORKSPACE, ARCH, HIP = range(7)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smla_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from sparse_mla_attention_smla_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_header_and_binding_agree(lib):
+    names = declared_functions()
+    assert len(names) == 13
+    assert sorted(B.EXPORTED) == names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert getattr(lib, name) is not None
+    out = os.popen(f"nm -D --defined-only {B.LIB_PATH}").read()
+    for name in declared_functions():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_status_strings(lib):
+    for code, text in [(0, "ok"), (SHAPE, "unsupported shape"), (ARCH, "device is not gfx950"),
+                       (99, "unknown status")]:
+        assert B.status_string(code) == text
+
+
+def test_workspace_sizes(lib):
+    # headline shape: delta 2 MiB + dS/P 1 GiB + interm 2 GiB + CSR/gather scratch
+    n = lib.smla_bwd_workspace_bytes(4096, 128, 5120, 512)
+    assert 3.0 * 2 ** 30 < n < 3.2 * 2 ** 30
+    assert lib.smla_bwd_workspace_bytes(64, 24, 64, 16) == 0          # H % 16 != 0
+    assert lib.smla_bwd_workspace_bytes(64, 16, 63, 16) == 0          # num_kv < T
+    assert lib.smla_csr_workspace_bytes(64, 16, 64) > 0
+    assert lib.smla_gather_workspace_bytes(64, 16, 64) > 0
+    assert lib.smla_dsink_workspace_bytes(64, 16) == 2 * 16 * 4
+
+
+A = 0x10000000  # fake, 256-B aligned device addresses (never dereferenced)
+
+
+def _bwd(lib, T=64, H=16, N=64, K=16, scale=0.05, sink=True, d_sink=True, ws=1 << 34, **ptr):
+    p = dict(q=A, kv=2 * A, dO=3 * A, o=4 * A, lse=5 * A, idx=6 * A, sink=7 * A if sink else None,
+             dq=8 * A, dkv=9 * A, d_sink=10 * A if d_sink else None, n_inv=None, work=11 * A)
+    p.update(ptr)
+    return lib.smla_bwd(p["q"], p["kv"], p["dO"], p["o"], p["lse"], p["idx"], p["sink"], T, H, N, K,
+                        scale, p["dq"], p["dkv"], p["d_sink"], p["n_inv"], p["work"], ws, None)
+
+
+def test_bwd_argument_errors(lib):
+    assert _bwd(lib, H=24) == SHAPE
+    assert _bwd(lib, H=144) == SHAPE
+    assert _bwd(lib, K=0) == SHAPE
+    assert _bwd(lib, N=63) == SHAPE                       # num_kv < T
+    assert _bwd(lib, N=1 << 20) == SHAPE
+    assert _bwd(lib, T=1 << 20, N=1 << 20 - 1, K=4096) == SHAPE
+    assert _bwd(lib, scale=float("nan")) == INVALID
+    assert _bwd(lib, d_sink=False) == INVALID             # sink without d_sink
+    assert _bwd(lib, sink=False) == INVALID               # d_sink without sink
+    assert _bwd(lib, q=None) == INVALID
+    assert _bwd(lib, q=A + 2) == ALIGN
+    assert _bwd(lib, lse=5 * A + 2) == ALIGN
+    assert _bwd(lib, work=None) == WORKSPACE
+    assert _bwd(lib, ws=1024) == WORKSPACE
+    assert _bwd(lib, dq=A) == INVALID                     # dq aliases q
+    assert _bwd(lib, work=9 * A + 4096) == INVALID        # workspace inside dkv
+    # a valid call gets past validation and then needs a gfx950 device
+    assert _bwd(lib) in (HIP, ARCH)
+
+
+def test_stage_argument_errors(lib):
+    assert lib.smla_delta(A, 2 * A, 4, 16, A, None) == INVALID          # delta aliases o
+    assert lib.smla_delta(A, 2 * A, 4, 20, 3 * A, None) == SHAPE
+    assert lib.smla_delta(A + 8, 2 * A, 4, 16, 3 * A, None) == ALIGN
+    assert lib.smla_build_csr(A, 4, 16, 3, 2 * A, 3 * A, None, 4 * A, 1 << 30, None) == SHAPE
+    assert lib.smla_build_csr(A, 4, 16, 8, 2 * A, 3 * A, None, 4 * A, 8, None) == WORKSPACE
+    assert lib.smla_gather(A, 2 * A, 3 * A, 4, 16, 8, 4 * A, None, 0, None) == WORKSPACE
+    assert lib.smla_dsink(A, 2 * A, None, 4, 16, 3 * A, 4 * A, 1024, None) == INVALID
+    assert lib.smla_fwd(A, 2 * A, 3 * A, None, 4, 16, 8, 16, float("inf"), 4 * A, 5 * A, None) == INVALID
+    assert lib.smla_fwd(A, 2 * A, 3 * A, None, 4, 16, 8, 16, 0.1, A, 5 * A, None) == INVALID
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()

@@ -1,0 +1,332 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Every call goes through the C ABI (libsmla.so via the ctypes binding).  Inputs
+are the seeded workloads; O and lse come from the oracle forward, rounded the
+way the backward consumes them.  Bars: the CSR is bit-exact; dq, dkv, d_sink
+(and the bf16 stage tensors) within rel-L2 5e-3 and cosine 0.9999 of the oracle.
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import smla_oracle as orc
+from sparse_mla_attention_smla_amd import inputs
+from tests._helpers import (SCALE, assert_close, dev, dev_bf16, host_bf16, host_bits, rel_l2,
+                            workload, workload_nosink)
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - collected on CPU only with -m gpu
+    pytest.skip("no GPU", allow_module_level=True)
+
+from sparse_mla_attention_smla_amd import binding as B  # noqa: E402
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(x):
+    d = {k: dev_bf16(x[k]) for k in ("q", "kv", "dO", "O")}
+    d["idx"] = dev(x["idx"])
+    d["lse"] = dev(x["lse"])
+    d["sink"] = dev(x["sink"]) if x["sink"] is not None else None
+    return d
+
+
+def _run_bwd(d, **kw):
+    out = B.smla_bwd(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"], SCALE, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------------------
+# small workloads: full oracle, stage by stage
+# ---------------------------------------------------------------------------
+
+@pytest.fixture(scope="module", params=["tiny", "small", "small_nosink"])
+def small_case(request):
+    name = request.param
+    x = workload_nosink("small") if name == "small_nosink" else workload(name)
+    _say(f"[case] {name}: T={x['q'].shape[0]} H={x['q'].shape[1]} topk={x['idx'].shape[1]}")
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE,
+                       stages=True)
+    return name, x, ref, _to_dev(x)
+
+
+def test_end_to_end(small_case):
+    name, x, ref, d = small_case
+    dq, dkv, ds = _run_bwd(d)
+    assert_close(f"{name} dq", host_bf16(dq), ref["dq"])
+    assert_close(f"{name} dkv", host_bf16(dkv), ref["dkv"])
+    if x["sink"] is not None:
+        assert_close(f"{name} d_sink", ds.cpu().numpy(), ref["d_sink"])
+    else:
+        assert ds is None
+
+
+def test_stage_delta(small_case):
+    name, x, ref, d = small_case
+    delta = B.smla_delta(d["O"], d["dO"])
+    torch.cuda.synchronize()
+    assert rel_l2(delta.cpu().numpy(), ref["delta"]) < 1e-5
+
+
+def test_stage_dq_and_dsp(small_case):
+    name, x, ref, d = small_case
+    delta = dev(ref["delta"].astype(np.float32))
+    dq, dsp = B.smla_dq(d["q"], d["kv"], d["dO"], d["lse"], delta, d["idx"], SCALE)
+    torch.cuda.synchronize()
+    assert_close(f"{name} dq stage", host_bf16(dq), ref["dq"])
+    H = x["q"].shape[1]
+    got = host_bf16(dsp)                                   # [T, K, 2H]
+    valid = (x["idx"] >= 0) & (x["idx"] < x["kv"].shape[0])
+    want_ds = SCALE * ref["dS"].transpose(0, 2, 1)         # [T, K, H]
+    want_p = ref["P"].transpose(0, 2, 1)
+    assert_close(f"{name} scale*dS", got[..., :H][valid], want_ds[valid])
+    assert_close(f"{name} P", got[..., H:][valid], want_p[valid])
+    # masked slots inside tiles that hold a valid slot are exact zeros
+    K = x["idx"].shape[1]
+    for t in range(x["idx"].shape[0]):
+        for k0 in range(0, K, 32):
+            if valid[t, k0:k0 + 32].any():
+                m = ~valid[t, k0:k0 + 32]
+                assert np.all(got[t, k0:k0 + 32][m] == 0.0)
+
+
+def test_stage_interm(small_case):
+    name, x, ref, d = small_case
+    H = x["q"].shape[1]
+    T, K = x["idx"].shape
+    # dsp input from the oracle, rounded to bf16 as the kernel consumes it
+    dsp = np.concatenate([SCALE * ref["dS"].transpose(0, 2, 1), ref["P"].transpose(0, 2, 1)], axis=2)
+    dsp_bits = orc.f64_to_bf16_rne(dsp)
+    interm = B.smla_interm(d["q"], d["dO"], dev_bf16(dsp_bits), d["idx"], x["kv"].shape[0])
+    torch.cuda.synchronize()
+    got = host_bf16(interm).reshape(T, K, 512)
+    dsp64 = orc.bf16_to_f64(dsp_bits)
+    want = (np.matmul(dsp64[..., :H], orc.bf16_to_f64(x["q"])) +
+            np.matmul(dsp64[..., H:], orc.bf16_to_f64(x["dO"])))
+    valid = (x["idx"] >= 0) & (x["idx"] < x["kv"].shape[0])
+    assert_close(f"{name} interm", got[valid], want[valid])
+    # and against the oracle's own interm (through the rounded dsp)
+    assert_close(f"{name} interm vs oracle", got[valid], ref["interm"][valid])
+
+
+def test_stage_csr_bit_exact(small_case):
+    name, x, ref, d = small_case
+    N = x["kv"].shape[0]
+    row_ptr, slots, n_inv = B.smla_build_csr(d["idx"], N, count_invalid=True)
+    torch.cuda.synchronize()
+    rp, sl = orc.csr(x["idx"], N)
+    assert np.array_equal(row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(slots.cpu().numpy()[: rp[-1]], sl)
+    assert int(n_inv.item()) == orc.count_invalid(x["idx"], N)
+
+
+def test_stage_gather(small_case):
+    name, x, ref, d = small_case
+    T, K = x["idx"].shape
+    N = x["kv"].shape[0]
+    interm_bits = orc.f64_to_bf16_rne(ref["interm"])          # oracle interm, rounded
+    rp, sl = orc.csr(x["idx"], N)
+    dkv = B.smla_gather(dev_bf16(interm_bits.reshape(T * K, 512)), dev(rp), dev(sl), T, K, N)
+    torch.cuda.synchronize()
+    want = orc.dkv_from_interm(interm_bits, x["idx"], N)
+    assert_close(f"{name} gather", host_bf16(dkv), want, tol=3e-3)
+    unused = np.setdiff1d(np.arange(N), x["idx"][x["idx"] >= 0])
+    assert np.all(host_bf16(dkv)[unused] == 0.0)
+
+
+def test_stage_dsink(small_case):
+    name, x, ref, d = small_case
+    if x["sink"] is None:
+        pytest.skip("no sink in this case")
+    ds = B.smla_dsink(d["lse"], dev(ref["delta"].astype(np.float32)), d["sink"])
+    torch.cuda.synchronize()
+    assert rel_l2(ds.cpu().numpy(), ref["d_sink"]) < 1e-4
+
+
+def host_bits_t(t):
+    return t.view(torch.int16)
+
+
+def test_deterministic_and_poisoned_workspace(small_case):
+    name, x, ref, d = small_case
+    T, H, _ = x["q"].shape
+    N, K = x["kv"].shape[0], x["idx"].shape[1]
+    ws = torch.full((B.bwd_workspace_bytes(T, H, N, K),), 0xFF, dtype=torch.uint8, device="cuda")
+    a = _run_bwd(d, workspace=ws)
+    ws.fill_(0x00)
+    b = _run_bwd(d, workspace=ws)
+    ws.fill_(0x7F)
+    c = _run_bwd(d, workspace=ws)
+    for i in range(2):
+        assert torch.equal(host_bits_t(a[i]), host_bits_t(b[i])) and torch.equal(host_bits_t(a[i]), host_bits_t(c[i]))
+    if a[2] is not None:
+        assert torch.equal(a[2], b[2]) and torch.equal(a[2], c[2])
+
+
+# ---------------------------------------------------------------------------
+# forward (test-input producer)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,sink", [("tiny", True), ("small", True), ("small", False)])
+def test_forward_matches_oracle(name, sink):
+    x = inputs.make(name, sink=sink)
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    s = dev(x["sink"]) if sink else None
+    o, lse = B.smla_fwd(dev_bf16(x["q"]), dev_bf16(x["kv"]), dev(x["idx"]), s, SCALE)
+    torch.cuda.synchronize()
+    assert_close(f"{name} O", host_bf16(o), O64)
+    got = lse.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - lse64)) < 1e-4
+
+
+# ---------------------------------------------------------------------------
+# edge cases: ragged shapes, masks, empty inputs
+# ---------------------------------------------------------------------------
+
+def _custom(T, H, N, K, seed, sink=True, pool_frac=0.0):
+    rng = np.random.default_rng(seed)
+    idx = np.full((T, K), -1, dtype=np.int32)
+    for t in range(T):
+        n = int(rng.integers(0, K + 1))
+        cand = np.arange(min(N, max(1, t + 1 + int(pool_frac * (N - T)))))
+        n = min(n, cand.size)
+        idx[t, :n] = np.sort(rng.choice(cand, n, replace=False))
+    x = {"q": inputs.normal_bf16((T, H, 512), seed, 1), "kv": inputs.normal_bf16((N, 512), seed, 2),
+         "dO": inputs.normal_bf16((T, H, 512), seed, 3), "idx": idx,
+         "sink": rng.standard_normal(H).astype(np.float32) if sink else None}
+    return x
+
+
+def _oracle_inputs(x):
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    x["O"], x["lse"] = orc.emit_forward_outputs(O64, lse64)
+    return x
+
+
+@pytest.mark.parametrize("T,H,N,K,sink", [
+    (37, 48, 53, 40, True),     # 3-wave head groups, ragged 32-slot tail, pool rows
+    (20, 32, 20, 1, True),      # topk = 1
+    (33, 80, 40, 70, False),    # 1-wave head groups, no sink
+    (17, 112, 30, 33, True),
+    (9, 128, 300, 96, True),    # most kv rows unused
+])
+def test_ragged_shapes(T, H, N, K, sink):
+    x = _custom(T, H, N, K, seed=T * 1000 + H, sink=sink, pool_frac=0.5)
+    x["idx"][3] = -1                                    # one all-masked row
+    x = _oracle_inputs(x)
+    _say(f"[ragged] T={T} H={H} N={N} K={K} sink={sink}")
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE)
+    dq, dkv, ds = _run_bwd(_to_dev(x))
+    assert_close("dq", host_bf16(dq), ref["dq"])
+    assert_close("dkv", host_bf16(dkv), ref["dkv"])
+    assert np.all(host_bf16(dq)[3] == 0.0)
+    unused = np.setdiff1d(np.arange(N), x["idx"][x["idx"] >= 0])
+    assert np.all(host_bf16(dkv)[unused] == 0.0)
+    if sink:
+        assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
+
+
+def test_shuffled_slots_invalid_indices_and_padding():
+    x = dict(workload("small"))
+    idx = inputs.shuffle_slots(x["idx"], seed=5)
+    rng = np.random.default_rng(8)
+    bad = rng.random(idx.shape) < 0.01
+    idx = np.where(bad, np.where(rng.random(idx.shape) < 0.5, -7, x["kv"].shape[0] + 3), idx)
+    idx = np.concatenate([idx, np.full((idx.shape[0], 16), -1, np.int32)], axis=1).astype(np.int32)
+    x["idx"] = idx
+    x = _oracle_inputs(x)
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], idx, x["sink"], SCALE)
+    dq, dkv, ds, n_inv = _run_bwd(_to_dev(x), count_invalid=True)
+    assert_close("dq", host_bf16(dq), ref["dq"])
+    assert_close("dkv", host_bf16(dkv), ref["dkv"])
+    assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
+    assert int(n_inv.item()) == orc.count_invalid(idx, x["kv"].shape[0]) > 0
+    row_ptr, slots = B.smla_build_csr(dev(idx), x["kv"].shape[0])
+    rp, sl = orc.csr(idx, x["kv"].shape[0])
+    assert np.array_equal(row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(slots.cpu().numpy()[: rp[-1]], sl)
+
+
+def test_all_masked_without_sink_gives_zero():
+    x = _custom(16, 64, 40, 32, seed=3, sink=False)
+    x["idx"][:] = -1
+    x = _oracle_inputs(x)
+    assert np.all(np.isneginf(x["lse"]))
+    dq, dkv, ds = _run_bwd(_to_dev(x))
+    assert np.all(host_bf16(dq) == 0.0) and np.all(host_bf16(dkv) == 0.0)
+    o, lse = B.smla_fwd(dev_bf16(x["q"]), dev_bf16(x["kv"]), dev(x["idx"]), None, SCALE)
+    torch.cuda.synchronize()
+    assert np.all(host_bf16(o) == 0.0) and np.all(np.isneginf(lse.cpu().numpy()))
+
+
+def test_empty_T():
+    H, N, K = 64, 8, 16
+    z = lambda *s: torch.empty(s, dtype=torch.bfloat16, device="cuda")
+    sink = torch.randn(H, device="cuda")
+    dq, dkv, ds = B.smla_bwd(z(0, H, 512), torch.randn(N, 512, device="cuda").bfloat16(), z(0, H, 512),
+                             z(0, H, 512), torch.empty(0, H, device="cuda"),
+                             torch.empty(0, K, dtype=torch.int32, device="cuda"), sink, SCALE)
+    torch.cuda.synchronize()
+    assert torch.all(dkv.float() == 0) and torch.all(ds == 0)
+
+
+def test_error_codes_from_device_side_entry():
+    x = _to_dev(_oracle_inputs(_custom(8, 16, 8, 16, seed=1)))
+    with pytest.raises(B.SmlaError) as e:
+        B.smla_bwd(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE,
+                   workspace=torch.empty(16, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == 4
+    with pytest.raises(B.SmlaError) as e:
+        B.smla_bwd(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE,
+                   out=(x["q"], torch.empty_like(x["kv"]), torch.empty(16, device="cuda")))
+    assert e.value.status == 1   # dq aliases q
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads (the benchmark's launch configuration), sampled outputs
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["headline", "skewed", "long"])
+def test_full_size_sampled(name):
+    _say(f"[full] {name}: generating inputs and the oracle forward")
+    x = workload(name)
+    w = x["workload"]
+    d = _to_dev(x)
+    _say(f"[full] {name}: running smla_bwd")
+    dq, dkv, ds = _run_bwd(d)
+    # CSR: bit-exact at full size
+    row_ptr, slots = B.smla_build_csr(d["idx"], w.num_kv)
+    rp, sl = orc.csr(x["idx"], w.num_kv)
+    assert np.array_equal(row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(slots.cpu().numpy()[: rp[-1]], sl)
+    # dq on sampled tokens
+    rng = np.random.default_rng(w.index)
+    toks = sorted(set([0, 1, 127, 128, 1535, w.T // 2, w.T - 1] + list(rng.integers(0, w.T, 9))))
+    r = orc.backward_tokens(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, toks)
+    assert_close(f"{name} dq sampled", host_bf16(dq[toks]), r["dq"])
+    # dkv on sampled rows: token rows, the busiest pool row, a lightly used pool row
+    counts = np.diff(rp)
+    pool = np.arange(w.T, w.num_kv)
+    busiest = int(pool[np.argmax(counts[w.T:])])
+    light = int(pool[np.argmin(np.where(counts[w.T:] > 0, counts[w.T:], 1 << 30))])
+    rows = sorted(set([0, 5, w.T // 3, w.T - 1, busiest, light] + list(rng.integers(0, w.num_kv, 4))))
+    _say(f"[full] {name}: oracle dkv on rows {rows} (contributors {counts[rows].tolist()})")
+    want = orc.dkv_rows(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, rows)
+    assert_close(f"{name} dkv sampled", host_bf16(dkv[rows]), want)
+    empty = np.nonzero(counts == 0)[0]
+    if empty.size:
+        assert np.all(host_bf16(dkv[torch.as_tensor(empty[:64], device='cuda')]) == 0.0)
+    # d_sink: every token contributes
+    assert_close(f"{name} d_sink", ds.cpu().numpy(), orc.d_sink(x["dO"], x["O"], x["lse"], x["sink"]))
+    del d
+    torch.cuda.empty_cache()
