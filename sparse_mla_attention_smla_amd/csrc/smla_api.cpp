@@ -302,9 +302,10 @@ int smla_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* s
         return SMLA_ERR_ALIGN;
     const size_t need = gather_scratch_bytes(M, num_kv);
     if (workspace == nullptr || workspace_bytes < need) return SMLA_ERR_WORKSPACE;
+    // slots holds row_ptr[num_kv] entries, a device-side count: only its first entry is checked
     const Range all[] = {{interm, (size_t)M * kD * 2},
                          {row_ptr, (size_t)(num_kv + 1) * 4},
-                         {slots, (size_t)M * 4},
+                         {slots, 4},
                          {dkv, (size_t)num_kv * kD * 2},
                          {workspace, need}};
     if (!outputs_disjoint(all, 5, 3)) return SMLA_ERR_INVALID_ARG;
