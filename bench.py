@@ -169,7 +169,7 @@ def main():
 
     # ---- per-stage timing (each stage entry point alone, same stream, same buffers)
     delta = torch.empty((T, H), dtype=torch.float32, device="cuda")
-    dsp = torch.empty((T, K, 2 * H), dtype=torch.bfloat16, device="cuda")
+    dsp = torch.empty((B.dsp_numel(T, H, K),), dtype=torch.bfloat16, device="cuda")
     interm = torch.empty((T * K, D), dtype=torch.bfloat16, device="cuda")
     row_ptr = torch.empty(N + 1, dtype=torch.int32, device="cuda")
     slots = torch.empty(T * K, dtype=torch.int32, device="cuda")
@@ -204,7 +204,7 @@ def main():
     algo = {
         "delta": ("hbm", 2 * qb + T * H * 4),
         "dq": ("mfma", 6.0 * T * H * K * D),
-        "interm": ("hbm", 2 * qb + T * K * 2 * H * 2 + T * K * D * 2),
+        "interm": ("hbm", 2 * qb + nnz * 2 * H * 2 + nnz * D * 2),
         "gather": ("hbm", nnz * D * 2 + nnz * 4 + N * D * 2),
     }
     stage_rows = {}

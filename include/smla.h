@@ -127,21 +127,29 @@ int smla_delta(const uint16_t* o, const uint16_t* dO, int T, int H, float* delta
  * kv feeds both the S and dP products; the kernel also emits dS and P).
  *   q, dO bf16 [T,H,512]  kv bf16 [num_kv,512]  lse, delta float [T,H]  idx int32 [T,topk]
  *   dq  bf16 [T, H, 512] out
- *   dsp bf16 [T, topk, 2H] out: dsp[t,k,h] = scale*dS[t,h,k], dsp[t,k,H+h] = P[t,h,k].
- *       Masked slots hold 0 when the 32-slot tile containing them has a valid
- *       slot; tiles with no valid slot are left unwritten.
+ *   dsp bf16 out, smla_dsp_bytes() bytes: per token t, the valid slots of its
+ *       index row (in increasing slot order, taken in runs of 512 slots) are
+ *       grouped in tiles of 32; tile c of token t is the block
+ *       dsp[((t*ceil(topk/32) + c) * 2H + r) * 32 + j], r < 2H, j < 32, with
+ *       row r = h holding scale*dS[t,h,slot_j] and row r = H + h holding
+ *       P[t,h,slot_j]; columns past the last valid slot of a run hold 0, and
+ *       blocks past the token's last tile are left unwritten.
  */
 int smla_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const float* lse,
             const float* delta, const int32_t* idx, int T, int H, int num_kv, int topk,
             float scale, uint16_t* dq, uint16_t* dsp, void* stream);
 
+/* Bytes of the dsp buffer of smla_dq / smla_interm (0 on a shape error). */
+size_t smla_dsp_bytes(int T, int H, int topk);
+
 /*
  * smla_interm -- per-slot dKV intermediate, contracted over all heads.
  * Page: aiter PR 4766, Structure table, "dKV-interm" row, and the R_CHUNK note
  * (the intermediate is [T, topk, 512] bf16).
- *   q, dO bf16 [T,H,512]  dsp bf16 [T,topk,2H] (from smla_dq)  idx int32 [T,topk]
- *   interm bf16 [T*topk, 512] out: interm[t*topk+k] = sum_h dsp[t,k,h] q[t,h] + dsp[t,k,H+h] dO[t,h]
- *       Rows of tiles with no valid slot are left unwritten; the gather never reads them.
+ *   q, dO bf16 [T,H,512]  dsp (from smla_dq, same idx)  idx int32 [T,topk]
+ *   interm bf16 [T*topk, 512] out: for every valid slot (t,k),
+ *       interm[t*topk+k] = sum_h scale*dS[t,h,k] q[t,h] + P[t,h,k] dO[t,h];
+ *       rows of masked slots are left unwritten (the gather never reads them).
  */
 int smla_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* dsp, const int32_t* idx,
                 int T, int H, int num_kv, int topk, uint16_t* interm, void* stream);

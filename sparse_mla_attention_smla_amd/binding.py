@@ -41,6 +41,7 @@ _SIGNATURES = {
     "smla_build_csr": ([_P, _I, _I, _I, _P, _P, _P, _P, _Z, _P], _I),
     "smla_gather_workspace_bytes": ([_I, _I, _I], _Z),
     "smla_gather": ([_P, _P, _P, _I, _I, _I, _P, _P, _Z, _P], _I),
+    "smla_dsp_bytes": ([_I, _I, _I], _Z),
     "smla_dsink_workspace_bytes": ([_I, _I], _Z),
     "smla_dsink": ([_P, _P, _P, _I, _I, _P, _P, _Z, _P], _I),
 }
@@ -192,8 +193,14 @@ def smla_delta(o, dO, delta=None):
     return delta
 
 
+def dsp_numel(T, H, topk) -> int:
+    """bf16 elements of the dS/P block buffer of smla_dq / smla_interm."""
+    return lib().smla_dsp_bytes(T, H, topk) // 2
+
+
 def smla_dq(q, kv, dO, lse, delta, idx, scale=None, dsp=None, dq=None):
-    """Returns (dq bf16 [T,H,512], dsp bf16 [T,topk,2H]) with dsp = [scale*dS | P] per slot."""
+    """Returns (dq bf16 [T,H,512], dsp bf16 blocks): per token, compacted tiles of
+    32 valid slots, each a [2H][32] block (rows scale*dS then P)."""
     T, H, _ = q.shape
     N, K = kv.shape[0], idx.shape[1]
     for t, n, dt, sh in ((q, "q", torch.bfloat16, (T, H, D)), (kv, "kv", torch.bfloat16, (N, D)),
@@ -203,7 +210,7 @@ def smla_dq(q, kv, dO, lse, delta, idx, scale=None, dsp=None, dq=None):
     if dq is None:
         dq = torch.empty_like(q)
     if dsp is None:
-        dsp = torch.empty((T, K, 2 * H), dtype=torch.bfloat16, device=q.device)
+        dsp = torch.empty((dsp_numel(T, H, K),), dtype=torch.bfloat16, device=q.device)
     _check("smla_dq", lib().smla_dq(_ptr(q), _ptr(kv), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(idx),
                                     T, H, N, K, _default_scale(scale), _ptr(dq), _ptr(dsp),
                                     _stream(q.device)))
@@ -215,7 +222,7 @@ def smla_interm(q, dO, dsp, idx, num_kv, interm=None):
     K = idx.shape[1]
     _need(q, "q", torch.bfloat16, (T, H, D))
     _need(dO, "dO", torch.bfloat16, (T, H, D))
-    _need(dsp, "dsp", torch.bfloat16, (T, K, 2 * H))
+    _need(dsp, "dsp", torch.bfloat16, (dsp_numel(T, H, K),))
     _need(idx, "idx", torch.int32, (T, K))
     if interm is None:
         interm = torch.empty((T * K, D), dtype=torch.bfloat16, device=q.device)

@@ -1,107 +1,154 @@
 // Gathered kv tiles in LDS for the attention kernels (forward and dQ).
 //
-// A tile holds the kv rows of 32 consecutive index slots of one query token.
-// The same rows feed two MFMA contractions with different reduction axes:
-//   S^T = kv . q^T          reduces over d     -> needs rows with d contiguous
-//   dq^T = kv^T . dS^T      reduces over slots -> needs columns with slots contiguous
-// so the tile is written to LDS twice: row-major [32][520] (pad 8 bf16 per row:
-// consecutive rows land in different bank groups) and transposed [512][40]
-// (pad 8 bf16).  The transposed copy is produced in registers: every thread
-// loads the same 16-byte column chunk of 8 slots, swaps 16-bit lanes with
-// byte permutes, and writes 8 transposed 16-byte rows.
+// Per query token, the valid index slots (index in [0, num_kv)) are first
+// compacted in LDS, in increasing slot order, in chunks of up to kChunk slots:
+// masked slots are never loaded or computed.  The compacted list is walked in
+// tiles of 32 slots; every tile row (one kv row, 1 KiB of bf16) is copied from
+// global memory straight into LDS by a buffer load with LDS destination (no
+// register staging).  A ring of kNBuf tile buffers keeps kNBuf-1 tiles in
+// flight while one is computed.  Tail positions past the last valid slot are
+// loaded with an out-of-range offset: the buffer range check returns zeros.
+// The copies are issued from inline assembly and waited for with explicit
+// vmcnt counts: the compiler would otherwise drain every copy in flight before
+// any LDS read, since it cannot tell the ring's buffers apart.
 //
-// Every wave-wide global load reads one whole 1 KiB kv row (64 lanes x 16 B).
-// Masked slots (index outside [0, num_kv)) are never read; they hold zeros.
+// The same LDS tile feeds two MFMA contractions with different reduction axes:
+//   S^T  = kv . q^T     reduces over d     -> ds_read_b128 of 8 d of one row
+//   dq^T = kv^T . dS^T  reduces over slots -> ds_read_b64_tr_b16: lane L of a
+//          16-lane group names row L/4, columns 4(L%4)..+3 and receives column
+//          L of those 4 consecutive rows (the transposed read of gfx950).
+// Rows are kRowPitch = 1072 bytes apart: 16 consecutive rows at one 16-byte
+// chunk fall in 16 distinct bank groups (first pattern) and 4 consecutive rows
+// x 32 bytes are disjoint (second pattern); every other offset is an immediate.
 #pragma once
 
 #include "smla_device.hpp"
 
 namespace smla {
 
-constexpr int kBK = 32;                                 // slots per tile
-constexpr int kRowStride = kD + 8;                      // bf16 per row-major row
-constexpr int kTrStride = kBK + 8;                      // bf16 per transposed row
-constexpr int kRowBytes = kBK * kRowStride * 2;         // 33,280
-constexpr int kTrBytes = kD * kTrStride * 2;            // 40,960
-constexpr int kTileBytes = kRowBytes + kTrBytes;        // 74,240
+constexpr int kBK = 32;                       // slots per tile
+constexpr int kRowPitch = kD * 2 + 48;        // 1072 bytes per tile row in LDS
+constexpr int kTileBytes = kBK * kRowPitch;   // 34,304 bytes
+constexpr int kNBuf = 4;                      // tile ring depth
+constexpr int kChunk = 512;                   // slots compacted at a time
 
-// 16-bit element e (0..7) of an 8 x bf16 chunk
-__device__ __forceinline__ uint32_t elem16(const u32x4& x, int e) {
-    const uint32_t w = x[e >> 1];
-    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// 32-bit LDS address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    // a C-style cast converts the generic pointer to the LDS address space
+    return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char*)p);
 }
 
-template <int NW>
-struct KvTile {
-    static constexpr int kGroups = kBK / 8;                      // groups of 8 slots
-    static constexpr int kGPT = (kGroups + NW - 1) / NW;         // groups per wave
-    u32x4 r[kGPT][8];
-    uint32_t mask;  // bit i: slot i of the tile addresses a kv row
+// 16 bytes per lane from the buffer at voffset into LDS at lds + 16*lane.
+// lds must be wave-uniform; it is moved to a scalar register first.
+__device__ __forceinline__ void copy_row_to_lds(i32x4 rsrc, uint32_t lds, int voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
+}
 
-    // Issue the global loads of tile `tile` (registers only, no LDS traffic).
-    __device__ __forceinline__ void load(const uint16_t* __restrict__ kv,
-                                         const int32_t* __restrict__ idx_row, int K, int N,
-                                         int tile, int w, int lane) {
-        const int slot = tile * kBK + lane;
-        const int v = (lane < kBK && slot < K) ? idx_row[slot] : -1;
-        mask = (uint32_t)__ballot(lane < kBK && valid_row(v, N));
-#pragma unroll
-        for (int gi = 0; gi < kGPT; ++gi) {
-            const int grp = w + gi * NW;
-            if (grp < kGroups) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int s = grp * 8 + i;
-                    const int row = __builtin_amdgcn_readlane(v, s);
-                    if ((mask >> s) & 1u)
-                        r[gi][i] = *reinterpret_cast<const u32x4*>(kv + (size_t)row * kD + lane * 8);
-                    else
-                        r[gi][i] = u32x4{0u, 0u, 0u, 0u};
-                }
-            }
-        }
-    }
+// Buffer resource over [p, p + bytes): loads outside the range return zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = (int32_t)(uint32_t)a;
+    r[1] = (int32_t)((a >> 32) & 0xFFFFu);   // stride 0
+    r[2] = (int32_t)bytes;                    // num_records (bytes)
+    r[3] = 0x00020000;                        // 32-bit data format, raw addressing
+    return r;
+}
+constexpr int kOobOffset = 0x7FFFFFF0;
 
-    // Write the loaded rows into one LDS tile buffer (both layouts).
-    __device__ __forceinline__ void store(char* buf, int w, int lane) const {
-        uint16_t* rowm = reinterpret_cast<uint16_t*>(buf);
-        uint16_t* tr = reinterpret_cast<uint16_t*>(buf + kRowBytes);
-#pragma unroll
-        for (int gi = 0; gi < kGPT; ++gi) {
-            const int grp = w + gi * NW;
-            if (grp < kGroups) {
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    *reinterpret_cast<u32x4*>(rowm + (grp * 8 + i) * kRowStride + lane * 8) = r[gi][i];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    u32x4 o;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        o[m] = elem16(r[gi][2 * m], e) | (elem16(r[gi][2 * m + 1], e) << 16);
-                    *reinterpret_cast<u32x4*>(tr + (lane * 8 + e) * kTrStride + grp * 8) = o;
-                }
-            }
-        }
-    }
+// vmcnt-only wait (expcnt and lgkmcnt left at their maxima), gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Compacted slot list of one chunk, in LDS.
+struct SlotList {
+    int32_t slot[kChunk];   // original slot index k
+    int32_t row[kChunk];    // kv row idx[t, k]
+    int32_t n;              // valid entries
 };
 
-// A operand of S^T = kv . q^T for slot sub-tile st (16 slots) and d-step ds (32 d).
-// Lane (c16, g): row = slot 16*st + c16, d = 32*ds + 8*g .. +7.
-__device__ __forceinline__ u32x4 tile_rows_a(const char* buf, int st, int ds, int c16, int g) {
-    const uint16_t* rowm = reinterpret_cast<const uint16_t*>(buf);
-    return *reinterpret_cast<const u32x4*>(rowm + (16 * st + c16) * kRowStride + 32 * ds + 8 * g);
+// Compact the valid slots of [k0, min(k0 + kChunk, K)) of one index row.
+// Run by one wave (64 lanes); the caller synchronises afterwards.
+__device__ __forceinline__ void compact_slots(const int32_t* __restrict__ idx_row, int K, int N, int k0,
+                                              SlotList* L, int lane) {
+    int v[kChunk / 64];
+#pragma unroll
+    for (int s = 0; s < kChunk / 64; ++s) {
+        const int k = k0 + 64 * s + lane;
+        v[s] = k < K ? idx_row[k] : -1;
+    }
+    int base = 0;
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+#pragma unroll
+    for (int s = 0; s < kChunk / 64; ++s) {
+        const bool ok = valid_row(v[s], N);
+        const uint64_t m = __ballot(ok);
+        if (ok) {
+            const int p = base + __popcll(m & below);
+            L->slot[p] = k0 + 64 * s + lane;
+            L->row[p] = v[s];
+        }
+        base += __popcll(m);
+    }
+    if (lane == 0) L->n = base;
+}
+
+// Issue the buffer->LDS copies of tile `ct` (compacted positions 32ct..32ct+31)
+// that belong to wave w of NW: rows w, w+NW, ...  Exactly 32/NW copies per wave.
+// buf is the LDS address of the ring buffer.
+template <int NW>
+__device__ __forceinline__ void issue_tile(i32x4 rsrc, const SlotList* L, int ct, uint32_t buf, int w,
+                                           int lane) {
+    static_assert(kBK % NW == 0, "rows per wave must be uniform");
+    const int n = L->n;
+#pragma unroll
+    for (int i = 0; i < kBK / NW; ++i) {
+        const int r = w + NW * i;
+        const int pos = ct * kBK + r;
+        const int row = pos < n ? L->row[pos] : -1;
+        const int voff = row >= 0 ? row * (kD * 2) + (lane << 4) : kOobOffset;
+        copy_row_to_lds(rsrc, buf + r * kRowPitch, voff);
+    }
+}
+
+// Per-lane byte offset of the S^T A operand inside a tile: lane (c16, g) reads
+// row 16*st + c16, elements d = 32*ds + 8g .. +7, i.e. rows_base + st*16*pitch + ds*64.
+__device__ __forceinline__ int rows_base(int c16, int g) { return c16 * kRowPitch + g * 16; }
+
+__device__ __forceinline__ u32x4 tile_rows_a(const char* buf, int base, int st, int ds) {
+    return *reinterpret_cast<const u32x4*>(buf + base + st * 16 * kRowPitch + ds * 64);
+}
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ u32x2 ds_read_tr16(const char* p) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
 }
 
 // A operand of X^T = kv^T . Y^T (reduction over the 32 slots) for d-tile dt.
-// Lane (c16, g): row d = 16*dt + c16; its 8 reduction elements are slots
-// 4g..4g+3 then 16+4g..16+4g+3 -- the same order in which the S^T accumulator
-// of sub-tiles 0 and 1 leaves them in the lane, so B = pack(acc0, acc1).
-__device__ __forceinline__ u32x4 tile_cols_a(const char* buf, int dt, int c16, int g) {
-    const uint16_t* tr = reinterpret_cast<const uint16_t*>(buf + kRowBytes);
-    const uint16_t* p = tr + (16 * dt + c16) * kTrStride + 4 * g;
-    const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-    const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 16);
+// Lane (c16, g) receives row d = 16*dt + c16 with slots 4g..4g+3 then
+// 16+4g..16+4g+3: the order in which the S^T accumulators of sub-tiles 0 and 1
+// leave them in the lane, so the matching B operand is pack(acc0, acc1).
+// Lane L = c16 of group g names row 4g + L/4 (then 16 + 4g + L/4) and columns
+// 16dt + 4(L%4) .. +3.
+__device__ __forceinline__ int cols_base(int c16, int g) {
+    return (4 * g + (c16 >> 2)) * kRowPitch + (c16 & 3) * 8;
+}
+
+__device__ __forceinline__ u32x4 tile_cols_a(const char* buf, int base, int dt) {
+    const u32x2 lo = ds_read_tr16(buf + base + dt * 32);
+    const u32x2 hi = ds_read_tr16(buf + base + 16 * kRowPitch + dt * 32);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 

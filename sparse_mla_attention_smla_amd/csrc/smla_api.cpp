@@ -67,6 +67,11 @@ smla_status check_shape(int T, int H, int num_kv, int topk) {
 
 smla_status hip_status(hipError_t e) { return e == hipSuccess ? SMLA_OK : SMLA_ERR_HIP; }
 
+// dS/P blocks: per token ceil(topk/32) blocks of [2H][32] bf16
+size_t dsp_bytes(int T, int H, int topk) {
+    return (size_t)T * (size_t)((topk + 31) / 32) * 2 * H * 32 * 2;
+}
+
 constexpr size_t kWsAlign = 256;
 
 struct BwdLayout {
@@ -83,7 +88,7 @@ BwdLayout bwd_layout(int T, int H, int num_kv, int topk) {
         return at;
     };
     L.delta = take((size_t)T * H * 4);
-    L.dsp = take((size_t)M * 2 * H * 2);
+    L.dsp = take(dsp_bytes(T, H, topk));
     L.interm = take((size_t)M * kD * 2);
     L.row_ptr = take((size_t)(num_kv + 1) * 4);
     L.slots = take((size_t)(M > 0 ? M : 1) * 4);
@@ -124,6 +129,11 @@ size_t smla_csr_workspace_bytes(int T, int topk, int num_kv) {
 size_t smla_gather_workspace_bytes(int T, int topk, int num_kv) {
     if (check_shape(T, 16, num_kv, topk) != SMLA_OK) return 0;
     return gather_scratch_bytes((int64_t)T * topk, num_kv);
+}
+
+size_t smla_dsp_bytes(int T, int H, int topk) {
+    if (check_shape(T, H, T > 0 ? T : 1, topk) != SMLA_OK) return 0;
+    return dsp_bytes(T, H, topk);
 }
 
 size_t smla_dsink_workspace_bytes(int T, int H) {
@@ -240,7 +250,7 @@ int smla_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const flo
     const Range all[] = {{q, qb},          {kv, (size_t)num_kv * kD * 2},
                          {dO, qb},         {lse, (size_t)T * H * 4},
                          {delta, (size_t)T * H * 4}, {idx, (size_t)T * topk * 4},
-                         {dq, qb},         {dsp, (size_t)T * topk * 2 * H * 2}};
+                         {dq, qb},         {dsp, dsp_bytes(T, H, topk)}};
     if (!outputs_disjoint(all, 8, 6)) return SMLA_ERR_INVALID_ARG;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_dq(q, kv, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dsp,
@@ -258,7 +268,7 @@ int smla_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* dsp, cons
     const size_t qb = (size_t)T * H * kD * 2;
     const Range all[] = {{q, qb},
                          {dO, qb},
-                         {dsp, (size_t)T * topk * 2 * H * 2},
+                         {dsp, dsp_bytes(T, H, topk)},
                          {idx, (size_t)T * topk * 4},
                          {interm, (size_t)T * topk * kD * 2}};
     if (!outputs_disjoint(all, 5, 4)) return SMLA_ERR_INVALID_ARG;

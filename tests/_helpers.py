@@ -84,3 +84,22 @@ def host_bf16(t) -> np.ndarray:
 def host_bits(t) -> np.ndarray:
     import torch
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def dsp_map(idx, num_kv, chunk=512, bk=32):
+    """Where each valid slot lives in the dS/P block buffer of smla_dq (the layout
+    documented in include/smla.h): per token, valid slots in increasing order,
+    in runs of `chunk` slots, grouped in tiles of `bk`.  Returns int arrays
+    (t, block, col, slot) with one entry per valid slot.  Pure index bookkeeping."""
+    T, K = idx.shape
+    ts, bs, cs, ks = [], [], [], []
+    for t in range(T):
+        c = 0
+        for k0 in range(0, K, chunk):
+            seg = np.arange(k0, min(k0 + chunk, K))
+            v = seg[(idx[t, seg] >= 0) & (idx[t, seg] < num_kv)]
+            pos = np.arange(v.size)
+            ts.append(np.full(v.size, t)); bs.append(c + pos // bk); cs.append(pos % bk); ks.append(v)
+            c += (v.size + bk - 1) // bk
+    cat = lambda a: np.concatenate(a) if a else np.zeros(0, int)
+    return cat(ts), cat(bs), cat(cs), cat(ks)

@@ -15,8 +15,8 @@ import pytest
 
 from oracle import smla_oracle as orc
 from sparse_mla_attention_smla_amd import inputs
-from tests._helpers import (SCALE, assert_close, dev, dev_bf16, host_bf16, host_bits, rel_l2,
-                            workload, workload_nosink)
+from tests._helpers import (SCALE, assert_close, dev, dev_bf16, dsp_map, host_bf16, host_bits,
+                            rel_l2, workload, workload_nosink)
 
 pytestmark = pytest.mark.gpu
 
@@ -84,39 +84,47 @@ def test_stage_dq_and_dsp(small_case):
     dq, dsp = B.smla_dq(d["q"], d["kv"], d["dO"], d["lse"], delta, d["idx"], SCALE)
     torch.cuda.synchronize()
     assert_close(f"{name} dq stage", host_bf16(dq), ref["dq"])
+    T, K = x["idx"].shape
     H = x["q"].shape[1]
-    got = host_bf16(dsp)                                   # [T, K, 2H]
-    valid = (x["idx"] >= 0) & (x["idx"] < x["kv"].shape[0])
-    want_ds = SCALE * ref["dS"].transpose(0, 2, 1)         # [T, K, H]
-    want_p = ref["P"].transpose(0, 2, 1)
-    assert_close(f"{name} scale*dS", got[..., :H][valid], want_ds[valid])
-    assert_close(f"{name} P", got[..., H:][valid], want_p[valid])
-    # masked slots inside tiles that hold a valid slot are exact zeros
-    K = x["idx"].shape[1]
-    for t in range(x["idx"].shape[0]):
-        for k0 in range(0, K, 32):
-            if valid[t, k0:k0 + 32].any():
-                m = ~valid[t, k0:k0 + 32]
-                assert np.all(got[t, k0:k0 + 32][m] == 0.0)
+    ntk = (K + 31) // 32
+    got = host_bf16(dsp).reshape(T, ntk, 2 * H, 32)
+    t, b, c, k = dsp_map(x["idx"], x["kv"].shape[0])
+    got_ds = got[t, b, :H, c]                              # [nnz, H]
+    got_p = got[t, b, H:, c]
+    assert_close(f"{name} scale*dS", got_ds, SCALE * ref["dS"][t, :, k])
+    assert_close(f"{name} P", got_p, ref["P"][t, :, k])
+    # tail columns of each token's last block of a run are exact zeros
+    filled = np.zeros((T, ntk, 32), bool)
+    filled[t, b, c] = True
+    used = np.zeros((T, ntk), bool)
+    used[t, b] = True
+    tail = used[:, :, None] & ~filled
+    assert np.all(got.transpose(0, 1, 3, 2)[tail] == 0.0)
 
 
 def test_stage_interm(small_case):
     name, x, ref, d = small_case
     H = x["q"].shape[1]
     T, K = x["idx"].shape
-    # dsp input from the oracle, rounded to bf16 as the kernel consumes it
-    dsp = np.concatenate([SCALE * ref["dS"].transpose(0, 2, 1), ref["P"].transpose(0, 2, 1)], axis=2)
-    dsp_bits = orc.f64_to_bf16_rne(dsp)
-    interm = B.smla_interm(d["q"], d["dO"], dev_bf16(dsp_bits), d["idx"], x["kv"].shape[0])
+    N = x["kv"].shape[0]
+    # dS/P blocks built from the oracle's P and dS (rounded to bf16 as consumed)
+    ntk = (K + 31) // 32
+    t, b, c, k = dsp_map(x["idx"], N)
+    blocks = np.zeros((T, ntk, 2 * H, 32))
+    blocks[t, b, :H, c] = SCALE * ref["dS"][t, :, k]
+    blocks[t, b, H:, c] = ref["P"][t, :, k]
+    bits = orc.f64_to_bf16_rne(blocks)
+    interm = B.smla_interm(d["q"], d["dO"], dev_bf16(bits.reshape(-1)), d["idx"], N)
     torch.cuda.synchronize()
     got = host_bf16(interm).reshape(T, K, 512)
-    dsp64 = orc.bf16_to_f64(dsp_bits)
-    want = (np.matmul(dsp64[..., :H], orc.bf16_to_f64(x["q"])) +
-            np.matmul(dsp64[..., H:], orc.bf16_to_f64(x["dO"])))
-    valid = (x["idx"] >= 0) & (x["idx"] < x["kv"].shape[0])
-    assert_close(f"{name} interm", got[valid], want[valid])
-    # and against the oracle's own interm (through the rounded dsp)
-    assert_close(f"{name} interm vs oracle", got[valid], ref["interm"][valid])
+    blk64 = orc.bf16_to_f64(bits)
+    dsk = blk64[t, b, :H, c]                               # [nnz, H]
+    pk = blk64[t, b, H:, c]
+    q64, dO64 = orc.bf16_to_f64(x["q"]), orc.bf16_to_f64(x["dO"])
+    want = np.einsum("nh,nhd->nd", dsk, q64[t]) + np.einsum("nh,nhd->nd", pk, dO64[t])
+    assert_close(f"{name} interm", got[t, k], want)
+    # and against the oracle's own interm (through the rounded blocks)
+    assert_close(f"{name} interm vs oracle", got[t, k], ref["interm"][t, k])
 
 
 def test_stage_csr_bit_exact(small_case):
