@@ -41,7 +41,13 @@ def parse():
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--stage-steps", type=int, default=10)
+    ap.add_argument("--mode", choices=["full", "profile"], default="full",
+                    help="profile: only the timed backward calls, then a plain device copy of "
+                         "COPY_BYTES (the reference for scaling HBM byte counters); prints no JSON")
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 30
 
 
 def kernel_source_hash() -> str:
@@ -166,6 +172,15 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     print(f"[bench] {ms:.3f} ms/call, {tflops:.1f} TFLOPS (wall {wall * 1e3 / args.steps:.3f} ms)",
           file=sys.stderr, flush=True)
+    if args.mode == "profile":
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] profile mode: {args.steps} backward calls, then {args.steps} copies of "
+              f"{COPY_BYTES} bytes", file=sys.stderr, flush=True)
+        return
 
     # ---- per-stage timing (each stage entry point alone, same stream, same buffers)
     delta = torch.empty((T, H), dtype=torch.float32, device="cuda")

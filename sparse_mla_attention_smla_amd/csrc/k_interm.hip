@@ -10,12 +10,12 @@
 // both terms of every slot's row:
 //   interm^T [512 x slots] = X^T . Y_t        (reduction over r in [0, 2H))
 // Work unit: one token per workgroup of 8 waves; wave w owns d in [64w, 64w+64).
-// X^T fragments (MFMA A operands: one d row, 8 consecutive r) are built once
-// per token with transposed LDS reads and stay in registers.  The token's
-// valid slots are compacted exactly as in the dQ kernel, so its dsp blocks
-// line up with the compacted tiles; each 32-slot block streams through a
-// 3-deep LDS ring, one tile of global loads in flight.  Rows of masked slots
-// are not written: the gather never reads them.
+// X^T fragments (MFMA A operands: one d row, 8 values of r) are built once per
+// token with transposed LDS reads and stay in registers.  The token's valid
+// slots are compacted exactly as in the dQ kernel, so its dsp blocks line up
+// with the compacted tiles; each 32-slot block streams through a 2-deep LDS
+// ring (rows padded to 96 bytes), one tile of loads in flight.  Rows of masked
+// slots are not written: the gather never reads them.
 #include "kv_tile.hpp"
 #include "smla_launch.hpp"
 
@@ -25,9 +25,9 @@ namespace {
 constexpr int kIWaves = 8;
 constexpr int kIThreads = kIWaves * 64;
 constexpr int kStageRows = 64;                          // X rows staged per pass
-constexpr int kStageBytes = kStageRows * kRowPitch;     // 68,608
-constexpr int kYPitch = kBK * 2;                        // 64 bytes per Y row (32 slots)
-constexpr int kYRing = 3;
+constexpr int kStageBytes = kStageRows * kRowPitch;     // 67,584
+constexpr int kYPitch = 96;                             // Y row: 32 slots (64 B) + 32 B pad
+constexpr int kYRing = 2;
 }  // namespace
 
 // NKS = 2H / 32 reduction steps (H = 16 * NKS)
@@ -38,8 +38,8 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     int N, int K, uint16_t* __restrict__ interm) {
     constexpr int H = NKS * 16;
     constexpr int R = 2 * H;
-    constexpr int kYBytes = R * kYPitch;                 // one dsp block
-    constexpr int kYChunks = kYBytes / 16;
+    constexpr int kYBytes = R * kYPitch;                 // one dsp block in LDS (padded rows)
+    constexpr int kYChunks = R * kBK * 2 / 16;           // 16-B chunks of one dsp block
     constexpr int kYPT = (kYChunks + kIThreads - 1) / kIThreads;
     static_assert(kYRing * kYBytes <= kStageBytes, "Y ring must fit in the staging area");
     __shared__ __attribute__((aligned(16))) char smem[kStageBytes];
@@ -53,10 +53,13 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int32_t* idx_row = idx + (size_t)t * K;
     if (w == 0) compact_slots(idx_row, K, N, 0, &L, lane);
 
-    // ---- X^T fragments: xf[dt][ks] = X[32ks + 8g .. +7][64w + 16dt + c16]
-    // (lane L of group g names staged row 8g + L/4 (+4), columns 64w + 16dt + 4(L%4))
+    // ---- X^T fragments: xf[dt][ks] holds column 64w + 16dt + c16 of X rows
+    // 32ks + 4g .. +3, then 32ks + 16 + 4g .. +3 (the reduction order shared with
+    // the Y operand).  Lane L of group g names staged row 4g + L/4 (then +16),
+    // columns 64w + 16dt + 4(L%4): 16 consecutive rows per read, which with an
+    // odd-multiple-of-32 pitch is free of LDS bank conflicts.
     u32x4 xf[4][NKS];
-    const int xb = (8 * g + (c16 >> 2)) * kRowPitch + (64 * w + 4 * (c16 & 3)) * 2;
+    const int xb = (4 * g + (c16 >> 2)) * kRowPitch + (64 * w + 4 * (c16 & 3)) * 2;
     for (int c0 = 0; c0 < R; c0 += kStageRows) {
 #pragma unroll
         for (int i = 0; i < kStageRows * (kD / 8) / kIThreads; ++i) {
@@ -78,7 +81,7 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
                     const u32x2 lo = ds_read_tr16(p + dt * 32);
-                    const u32x2 hi = ds_read_tr16(p + 4 * kRowPitch + dt * 32);
+                    const u32x2 hi = ds_read_tr16(p + 16 * kRowPitch + dt * 32);
                     xf[dt][ks] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
             }
@@ -89,8 +92,9 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // ---- stream the Y tiles (one dsp block per compacted tile)
     const int ntk = (K + kBK - 1) / kBK;
     const uint16_t* ytok = dsp + (size_t)t * ntk * R * kBK;
-    // B operand: lane L of group g names Y row 32ks + 8g + L/4 (+4), columns 16sst + 4(L%4)
-    const int yb = (8 * g + (c16 >> 2)) * kYPitch + (c16 & 3) * 8;
+    // B operand: lane L of group g names Y row 32ks + 4g + L/4 (then +16),
+    // columns 16sst + 4(L%4)
+    const int yb = (4 * g + (c16 >> 2)) * kYPitch + (c16 & 3) * 8;
     u32x4 pre[kYPT];
     auto load_tile = [&](int ct) {
         const uint16_t* src = ytok + (size_t)ct * R * kBK;
@@ -104,7 +108,8 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
         for (int i = 0; i < kYPT; ++i) {
             const int id = tid + kIThreads * i;
-            if (id < kYChunks) *reinterpret_cast<u32x4*>(yb_lds + id * 16) = pre[i];
+            if (id < kYChunks)
+                *reinterpret_cast<u32x4*>(yb_lds + (id >> 2) * kYPitch + (id & 3) * 16) = pre[i];
         }
     };
 
@@ -135,7 +140,7 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     for (int ks = 0; ks < NKS; ++ks) {
                         const char* p = ybuf + yb + ks * 32 * kYPitch + sst * 32;
                         const u32x2 lo = ds_read_tr16(p);
-                        const u32x2 hi = ds_read_tr16(p + 4 * kYPitch);
+                        const u32x2 hi = ds_read_tr16(p + 16 * kYPitch);
                         cacc = mfma16(xf[dt][ks], u32x4{lo[0], lo[1], hi[0], hi[1]}, cacc);
                     }
                     if (pos < n) {
