@@ -24,27 +24,13 @@
 
 namespace smla {
 
-// vmcnt allowed while waiting for tile `it`: DMA copies of the two tiles issued
-// after it (2R) plus the dS/P stores (S per tile) of up to three iterations.
-template <int R, int S>
-__device__ __forceinline__ void wait_tile(int it) {
-    constexpr int a0 = (2 * R) < 63 ? 2 * R : 63;
-    constexpr int a1 = (2 * R + S) < 63 ? 2 * R + S : 63;
-    constexpr int a2 = (2 * R + 2 * S) < 63 ? 2 * R + 2 * S : 63;
-    constexpr int a3 = (2 * R + 3 * S) < 63 ? 2 * R + 3 * S : 63;
-    if (it == 0) wait_vmcnt<a0>();
-    else if (it == 1) wait_vmcnt<a1>();
-    else if (it == 2) wait_vmcnt<a2>();
-    else wait_vmcnt<a3>();
-}
-
 template <int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
 void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 const uint16_t* __restrict__ dO, const float* __restrict__ lse,
                 const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
                 int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
-    static_assert(kNBuf == 4, "wait_tile assumes a 4-deep ring");
+    static_assert(kNBuf == 4, "the vmcnt bounds below assume a 4-deep ring");
     constexpr int R = kBK / NW;   // DMA copies per wave per tile
     constexpr int S = 4;          // dS/P stores per wave per tile
     __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
@@ -81,6 +67,13 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Software pipeline over the compacted tiles of a chunk.  Iteration j
+    // turns tile j's S/dP accumulators into P and dS (VALU, stores), then runs
+    // one unrolled block that interleaves the dq MFMAs of tile j with the S/dP
+    // MFMAs of tile j+1: two independent MFMA chains hide each other's LDS read
+    // latency.  Tile j+3 is copied into the ring slot tile j-1 used.
+    // VMEM ops per wave: R copies per tile, 4 dS/P stores per tile; the vmcnt
+    // bound when waiting for tile j+1 counts the ops issued after its copies.
     int ctg = 0;  // compacted tiles of earlier chunks
     for (int k0 = 0; k0 < K; k0 += kChunk) {
         if (k0 > 0 && w == 0) compact_slots(idx_row, K, N, k0, &L, lane);
@@ -89,46 +82,75 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         const int ntile = (n + kBK - 1) / kBK;
 #pragma unroll
         for (int p = 0; p < kNBuf - 1; ++p) issue_tile<NW>(rsrc, &L, p, ring + p * kTileBytes, w, lane);
-        for (int it = 0; it < ntile; ++it) {
-            wait_tile<R, S>(it);
-            __syncthreads();  // tile `it` landed for every wave; buffer (it-1)%4 is free
-            issue_tile<NW>(rsrc, &L, it + kNBuf - 1, ring + ((it + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
-            const char* buf = tiles + (it % kNBuf) * kTileBytes;
-
+        if (ntile > 0) {
             f32x4 sacc[2], pacc[2];
+            wait_vmcnt<(2 * R < 63 ? 2 * R : 63)>();
+            __syncthreads();
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
                 pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ds = 0; ds < 16; ++ds) {
-                    const u32x4 a = tile_rows_a(buf, rb, st, ds);
+                    const u32x4 a = tile_rows_a(tiles, rb, st, ds);
                     sacc[st] = mfma16(a, qf[ds], sacc[st]);
                     pacc[st] = mfma16(a, dof[ds], pacc[st]);
                 }
             }
-            float dss[2][4], ps[2][4];
+            // P and scale*dS of tile j from its accumulators; stores; B operand of dq
+            auto softmax_grad = [&](int j) -> u32x4 {
+                float dss[2][4], ps[2][4];
 #pragma unroll
-            for (int st = 0; st < 2; ++st)
+                for (int st = 0; st < 2; ++st)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const bool v = it * kBK + 16 * st + 4 * g + j < n;
-                    const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[st][j], c, -bias)) : 0.f;
-                    ps[st][j] = p;
-                    dss[st][j] = p * (pacc[st][j] - dl) * scale;
+                    for (int i = 0; i < 4; ++i) {
+                        const bool v = j * kBK + 16 * st + 4 * g + i < n;
+                        const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[st][i], c, -bias)) : 0.f;
+                        ps[st][i] = p;
+                        dss[st][i] = p * (pacc[st][i] - dl) * scale;
+                    }
+                uint16_t* blk = dsp_tok + (size_t)(ctg + j) * (2 * H) * kBK;
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    *reinterpret_cast<u32x2*>(blk + (size_t)h * kBK + 16 * st + 4 * g) =
+                        u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])};
+                    *reinterpret_cast<u32x2*>(blk + (size_t)(H + h) * kBK + 16 * st + 4 * g) =
+                        u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])};
                 }
-            uint16_t* blk = dsp_tok + (size_t)(ctg + it) * (2 * H) * kBK;
+                return u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
+                             pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
+            };
+            for (int j = 0; j + 1 < ntile; ++j) {
+                if (j == 0) wait_vmcnt<(R < 63 ? R : 63)>();
+                else if (j == 1) wait_vmcnt<(R + S < 63 ? R + S : 63)>();
+                else wait_vmcnt<(R + 2 * S < 63 ? R + 2 * S : 63)>();
+                __syncthreads();  // tile j+1 landed everywhere; ring slot of tile j-1 is free
+                issue_tile<NW>(rsrc, &L, j + kNBuf - 1, ring + ((j + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
+                const u32x4 bf = softmax_grad(j);
+                const char* bufa = tiles + (j % kNBuf) * kTileBytes;
+                const char* bufb = tiles + ((j + 1) % kNBuf) * kTileBytes;
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                *reinterpret_cast<u32x2*>(blk + (size_t)h * kBK + 16 * st + 4 * g) =
-                    u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])};
-                *reinterpret_cast<u32x2*>(blk + (size_t)(H + h) * kBK + 16 * st + 4 * g) =
-                    u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])};
+                for (int st = 0; st < 2; ++st) {
+                    sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int ds = 0; ds < 16; ++ds) {
+                    acc[2 * ds] = mfma16(tile_cols_a(bufa, cb, 2 * ds), bf, acc[2 * ds]);
+                    acc[2 * ds + 1] = mfma16(tile_cols_a(bufa, cb, 2 * ds + 1), bf, acc[2 * ds + 1]);
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
+                        const u32x4 a = tile_rows_a(bufb, rb, st, ds);
+                        sacc[st] = mfma16(a, qf[ds], sacc[st]);
+                        pacc[st] = mfma16(a, dof[ds], pacc[st]);
+                    }
+                }
             }
-            const u32x4 bf = {pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
-                              pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
+            const int jl = ntile - 1;
+            const u32x4 bf = softmax_grad(jl);
+            const char* bufl = tiles + (jl % kNBuf) * kTileBytes;
 #pragma unroll
-            for (int dt = 0; dt < 32; ++dt) acc[dt] = mfma16(tile_cols_a(buf, cb, dt), bf, acc[dt]);
+            for (int dt = 0; dt < 32; ++dt) acc[dt] = mfma16(tile_cols_a(bufl, cb, dt), bf, acc[dt]);
         }
         ctg += ntile;
         wait_vmcnt<0>();   // the ring's trailing copies land before LDS is reused
@@ -140,6 +162,170 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     for (int dt = 0; dt < 32; ++dt) {
         const u32x2 v = {pack_bf16(acc[dt][0], acc[dt][1]), pack_bf16(acc[dt][2], acc[dt][3])};
         *reinterpret_cast<u32x2*>(dq + qrow + 16 * dt + 4 * g) = v;
+    }
+}
+
+// Producer/consumer variant for 64-head groups (H % 64 == 0): 8 waves, two per
+// SIMD, so one wave's LDS and barrier waits are covered by the other's MFMAs.
+//   producers (waves 0-3): 16 heads each; q and dO in registers; S^T, dP^T of
+//     a tile, then P and scale*dS (stored as dsp blocks) and the dS fragment,
+//     published in LDS;
+//   consumers (waves 4-7): 32 heads x 256 d of the dq accumulator each; every
+//     transposed kv read feeds two MFMAs (the two head groups of the pair).
+// Producers run one tile ahead of consumers; one barrier per tile orders the
+// kv ring, the dS fragments (double-buffered) and the ring slot reuse.
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                   const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                   const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
+                   int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
+    static_assert(kNBuf == 4, "the vmcnt bounds below assume a 4-deep ring");
+    constexpr int NWAVES = 8;
+    constexpr int R = kBK / NWAVES;   // copies per wave per tile
+    constexpr int S = 4;              // dS/P stores per producer per tile
+    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    __shared__ SlotList L;
+    __shared__ u32x4 dsfrag[2][4][64];  // dS fragments: [slot parity][producer][lane]
+
+    const int nhg = H / 64;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int t = logical / nhg;
+    const int hg = logical - t * nhg;
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
+    const int32_t* idx_row = idx + (size_t)t * K;
+    if (w == 0) compact_slots(idx_row, K, N, 0, &L, lane);
+    const i32x4 rsrc = make_rsrc(kv, (uint32_t)N * (kD * 2));
+    const uint32_t ring = lds_addr(tiles);
+    const int ntk = (K + kBK - 1) / kBK;
+
+    if (w < 4) {
+        // ------------------------------------------------------------ producer
+        const int h = hg * 64 + w * 16 + c16;
+        const size_t qrow = ((size_t)t * H + h) * kD;
+        u32x4 qf[16], dof[16];
+#pragma unroll
+        for (int ds = 0; ds < 16; ++ds) {
+            qf[ds] = *reinterpret_cast<const u32x4*>(q + qrow + 32 * ds + 8 * g);
+            dof[ds] = *reinterpret_cast<const u32x4*>(dO + qrow + 32 * ds + 8 * g);
+        }
+        const float lse_h = lse[(size_t)t * H + h];
+        const float bias = (lse_h == -INFINITY) ? INFINITY : lse_h * kLog2e;
+        const float c = scale * kLog2e;
+        const float dl = delta[(size_t)t * H + h];
+        const int rb = rows_base(c16, g);
+        uint16_t* dsp_tok = dsp + (size_t)t * ntk * (2 * H) * kBK;
+        int ctg = 0;
+        for (int k0 = 0; k0 < K; k0 += kChunk) {
+            if (k0 > 0 && w == 0) compact_slots(idx_row, K, N, k0, &L, lane);
+            __syncthreads();
+            const int n = L.n;
+            const int ntile = (n + kBK - 1) / kBK;
+#pragma unroll
+            for (int p = 0; p < kNBuf - 1; ++p)
+                issue_tile<NWAVES>(rsrc, &L, p, ring + p * kTileBytes, w, lane);
+            // S^T, dP^T of tile j -> P, scale*dS (stored) -> dS fragment into LDS
+            auto produce = [&](int j) {
+                const char* buf = tiles + (j % kNBuf) * kTileBytes;
+                f32x4 sacc[2], pacc[2];
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ds = 0; ds < 16; ++ds) {
+                        const u32x4 a = tile_rows_a(buf, rb, st, ds);
+                        sacc[st] = mfma16(a, qf[ds], sacc[st]);
+                        pacc[st] = mfma16(a, dof[ds], pacc[st]);
+                    }
+                }
+                float dss[2][4], ps[2][4];
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool v = j * kBK + 16 * st + 4 * g + i < n;
+                        const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[st][i], c, -bias)) : 0.f;
+                        ps[st][i] = p;
+                        dss[st][i] = p * (pacc[st][i] - dl) * scale;
+                    }
+                uint16_t* blk = dsp_tok + (size_t)(ctg + j) * (2 * H) * kBK;
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    *reinterpret_cast<u32x2*>(blk + (size_t)h * kBK + 16 * st + 4 * g) =
+                        u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])};
+                    *reinterpret_cast<u32x2*>(blk + (size_t)(H + h) * kBK + 16 * st + 4 * g) =
+                        u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])};
+                }
+                dsfrag[j & 1][w][lane] =
+                    u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
+                          pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
+            };
+            if (ntile > 0) {
+                wait_vmcnt<2 * R>();
+                __syncthreads();
+                produce(0);
+                for (int j = 0; j < ntile; ++j) {
+                    if (j + 1 < ntile) {
+                        if (j == 0) wait_vmcnt<R + S>();
+                        else wait_vmcnt<R + 2 * S>();
+                    }
+                    __syncthreads();
+                    issue_tile<NWAVES>(rsrc, &L, j + kNBuf - 1,
+                                       ring + ((j + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
+                    if (j + 1 < ntile) produce(j + 1);
+                }
+            }
+            ctg += ntile;
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+    } else {
+        // ------------------------------------------------------------ consumer
+        const int cw = w - 4, hp = cw >> 1, dh = cw & 1;
+        const int cb = cols_base(c16, g);
+        f32x4 acc[16][2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < K; k0 += kChunk) {
+            __syncthreads();
+            const int n = L.n;
+            const int ntile = (n + kBK - 1) / kBK;
+#pragma unroll
+            for (int p = 0; p < kNBuf - 1; ++p)
+                issue_tile<NWAVES>(rsrc, &L, p, ring + p * kTileBytes, w, lane);
+            if (ntile > 0) {
+                wait_vmcnt<2 * R>();
+                __syncthreads();
+                for (int j = 0; j < ntile; ++j) {
+                    if (j + 1 < ntile) wait_vmcnt<R>();
+                    __syncthreads();
+                    issue_tile<NWAVES>(rsrc, &L, j + kNBuf - 1,
+                                       ring + ((j + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
+                    const u32x4 b0 = dsfrag[j & 1][2 * hp][lane];
+                    const u32x4 b1 = dsfrag[j & 1][2 * hp + 1][lane];
+                    const char* buf = tiles + (j % kNBuf) * kTileBytes;
+#pragma unroll
+                    for (int dt = 0; dt < 16; ++dt) {
+                        const u32x4 a = tile_cols_a(buf, cb, 16 * dh + dt);
+                        acc[dt][0] = mfma16(a, b0, acc[dt][0]);
+                        acc[dt][1] = mfma16(a, b1, acc[dt][1]);
+                    }
+                }
+            }
+            wait_vmcnt<0>();
+            __syncthreads();
+        }
+        // lane holds dq^T rows d = 256dh + 16dt + 4g .. +3 of head 32hp + 16m + c16
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int h = hg * 64 + 32 * hp + 16 * m + c16;
+            uint16_t* out = dq + ((size_t)t * H + h) * kD + 256 * dh + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < 16; ++dt)
+                *reinterpret_cast<u32x2*>(out + 16 * dt) =
+                    u32x2{pack_bf16(acc[dt][m][0], acc[dt][m][1]), pack_bf16(acc[dt][m][2], acc[dt][m][3])};
+        }
     }
 }
 
@@ -157,7 +343,7 @@ hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, 
     const int nw = dq_waves(H);
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
     switch (nw) {
-        case 4: smla_k2_dq<4><<<blocks, 256, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp); break;
+        case 4: smla_k2_dq_pc<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp); break;
         case 2: smla_k2_dq<2><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp); break;
         default: smla_k2_dq<1><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp); break;
     }

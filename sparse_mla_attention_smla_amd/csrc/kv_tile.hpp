@@ -62,7 +62,9 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
     r[3] = 0x00020000;                        // 32-bit data format, raw addressing
     return r;
 }
-constexpr int kOobOffset = 0x7FFFFFF0;
+// A row index whose byte offset (row * 1024 + lane * 16 < 2^31) lies beyond any
+// kv buffer (num_kv < 2^20, so its range is below 2^30 bytes).
+constexpr int kOobRow = (1 << 21) - 1;
 
 // vmcnt-only wait (expcnt and lgkmcnt left at their maxima), gfx9 encoding.
 template <int N>
@@ -111,14 +113,20 @@ template <int NW>
 __device__ __forceinline__ void issue_tile(i32x4 rsrc, const SlotList* L, int ct, uint32_t buf, int w,
                                            int lane) {
     static_assert(kBK % NW == 0, "rows per wave must be uniform");
+    constexpr int kR = kBK / NW;
     const int n = L->n;
+    // Lane i < kR fetches the kv row of copy i in one vector LDS read; tail
+    // positions map to a row whose offset is past any buffer range (the range
+    // check then yields zeros).  readlane hands each copy its row without
+    // branches, so all copies issue back to back.
+    const int lp = lane < kR ? lane : 0;
+    const int pos = ct * kBK + w + NW * lp;
+    const int rowv = L->row[pos < kChunk ? pos : kChunk - 1];
+    const int rowsel = pos < n ? rowv : kOobRow;
 #pragma unroll
-    for (int i = 0; i < kBK / NW; ++i) {
-        const int r = w + NW * i;
-        const int pos = ct * kBK + r;
-        const int row = pos < n ? L->row[pos] : -1;
-        const int voff = row >= 0 ? row * (kD * 2) + (lane << 4) : kOobOffset;
-        copy_row_to_lds(rsrc, buf + r * kRowPitch, voff);
+    for (int i = 0; i < kR; ++i) {
+        const int row = __builtin_amdgcn_readlane(rowsel, i);
+        copy_row_to_lds(rsrc, buf + (w + NW * i) * kRowPitch, row * (kD * 2) + (lane << 4));
     }
 }
 
