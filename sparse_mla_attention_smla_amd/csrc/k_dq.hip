@@ -90,8 +90,11 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
             for (int st = 0; st < 2; ++st) {
                 sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
                 pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-                for (int ds = 0; ds < 16; ++ds) {
+            for (int ds = 0; ds < 16; ++ds) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
                     const u32x4 a = tile_rows_a(tiles, rb, st, ds);
                     sacc[st] = mfma16(a, qf[ds], sacc[st]);
                     pacc[st] = mfma16(a, dof[ds], pacc[st]);
@@ -170,8 +173,11 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 //   producers (waves 0-3): 16 heads each; q and dO in registers; S^T, dP^T of
 //     a tile, then P and scale*dS (stored as dsp blocks) and the dS fragment,
 //     published in LDS;
-//   consumers (waves 4-7): 32 heads x 256 d of the dq accumulator each; every
-//     transposed kv read feeds two MFMAs (the two head groups of the pair).
+//   consumers (waves 4-7): all 64 heads x 128 d of the dq accumulator each;
+//     every transposed kv read feeds four MFMAs (one per head group), which
+//     halves the LDS instructions of the dq product.
+// Waves w and w+4 share a SIMD (measured on gfx950 from HW_ID), so each SIMD
+// runs one producer and one consumer.
 // Producers run one tile ahead of consumers; one barrier per tile orders the
 // kv ring, the dS fragments (double-buffered) and the ring slot reuse.
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
@@ -194,7 +200,8 @@ void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
     const int32_t* idx_row = idx + (size_t)t * K;
-    if (w == 0) compact_slots(idx_row, K, N, 0, &L, lane);
+    // a consumer wave compacts the slots while the producers load q and dO
+    if (w == 4) compact_slots(idx_row, K, N, 0, &L, lane);
     const i32x4 rsrc = make_rsrc(kv, (uint32_t)N * (kD * 2));
     const uint32_t ring = lds_addr(tiles);
     const int ntk = (K + kBK - 1) / kBK;
@@ -217,7 +224,6 @@ void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         uint16_t* dsp_tok = dsp + (size_t)t * ntk * (2 * H) * kBK;
         int ctg = 0;
         for (int k0 = 0; k0 < K; k0 += kChunk) {
-            if (k0 > 0 && w == 0) compact_slots(idx_row, K, N, k0, &L, lane);
             __syncthreads();
             const int n = L.n;
             const int ntile = (n + kBK - 1) / kBK;
@@ -227,13 +233,17 @@ void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
             // S^T, dP^T of tile j -> P, scale*dS (stored) -> dS fragment into LDS
             auto produce = [&](int j) {
                 const char* buf = tiles + (j % kNBuf) * kTileBytes;
+                // four independent accumulation chains (S and dP of both 16-slot halves)
                 f32x4 sacc[2], pacc[2];
 #pragma unroll
                 for (int st = 0; st < 2; ++st) {
                     sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
                     pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
 #pragma unroll
-                    for (int ds = 0; ds < 16; ++ds) {
+                for (int ds = 0; ds < 16; ++ds) {
+#pragma unroll
+                    for (int st = 0; st < 2; ++st) {
                         const u32x4 a = tile_rows_a(buf, rb, st, ds);
                         sacc[st] = mfma16(a, qf[ds], sacc[st]);
                         pacc[st] = mfma16(a, dof[ds], pacc[st]);
@@ -282,12 +292,15 @@ void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
         }
     } else {
         // ------------------------------------------------------------ consumer
-        const int cw = w - 4, hp = cw >> 1, dh = cw & 1;
+        const int dq4 = w - 4;  // d in [128 dq4, 128 dq4 + 128)
         const int cb = cols_base(c16, g);
-        f32x4 acc[16][2];
+        f32x4 acc[8][4];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[i][0] = acc[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int k0 = 0; k0 < K; k0 += kChunk) {
+            if (k0 > 0 && w == 4) compact_slots(idx_row, K, N, k0, &L, lane);
             __syncthreads();
             const int n = L.n;
             const int ntile = (n + kBK - 1) / kBK;
@@ -302,27 +315,28 @@ void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
                     __syncthreads();
                     issue_tile<NWAVES>(rsrc, &L, j + kNBuf - 1,
                                        ring + ((j + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
-                    const u32x4 b0 = dsfrag[j & 1][2 * hp][lane];
-                    const u32x4 b1 = dsfrag[j & 1][2 * hp + 1][lane];
+                    u32x4 b[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) b[m] = dsfrag[j & 1][m][lane];
                     const char* buf = tiles + (j % kNBuf) * kTileBytes;
 #pragma unroll
-                    for (int dt = 0; dt < 16; ++dt) {
-                        const u32x4 a = tile_cols_a(buf, cb, 16 * dh + dt);
-                        acc[dt][0] = mfma16(a, b0, acc[dt][0]);
-                        acc[dt][1] = mfma16(a, b1, acc[dt][1]);
+                    for (int dt = 0; dt < 8; ++dt) {
+                        const u32x4 a = tile_cols_a(buf, cb, 8 * dq4 + dt);
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) acc[dt][m] = mfma16(a, b[m], acc[dt][m]);
                     }
                 }
             }
             wait_vmcnt<0>();
             __syncthreads();
         }
-        // lane holds dq^T rows d = 256dh + 16dt + 4g .. +3 of head 32hp + 16m + c16
+        // lane holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int h = hg * 64 + 32 * hp + 16 * m + c16;
-            uint16_t* out = dq + ((size_t)t * H + h) * kD + 256 * dh + 4 * g;
+        for (int m = 0; m < 4; ++m) {
+            const int h = hg * 64 + 16 * m + c16;
+            uint16_t* out = dq + ((size_t)t * H + h) * kD + 128 * dq4 + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < 16; ++dt)
+            for (int dt = 0; dt < 8; ++dt)
                 *reinterpret_cast<u32x2*>(out + 16 * dt) =
                     u32x2{pack_bf16(acc[dt][m][0], acc[dt][m][1]), pack_bf16(acc[dt][m][2], acc[dt][m][3])};
         }

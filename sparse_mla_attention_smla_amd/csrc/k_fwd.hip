@@ -66,14 +66,19 @@ void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
             issue_tile<NW>(rsrc, &L, it + kNBuf - 1, ring + ((it + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
             const char* buf = tiles + (it % kNBuf) * kTileBytes;
 
-            f32x4 sacc[2];
+            // four accumulation chains: both 16-slot halves, even and odd d-steps
+            f32x4 sacc[2], sodd[2];
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int st = 0; st < 2; ++st) sacc[st] = sodd[st] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ds = 0; ds < 16; ++ds)
+            for (int ds = 0; ds < 16; ds += 2)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
                     sacc[st] = mfma16(tile_rows_a(buf, rb, st, ds), qf[ds], sacc[st]);
-            }
+                    sodd[st] = mfma16(tile_rows_a(buf, rb, st, ds + 1), qf[ds + 1], sodd[st]);
+                }
+#pragma unroll
+            for (int st = 0; st < 2; ++st) sacc[st] += sodd[st];
             float x[2][4];
             float tmax = -INFINITY;
 #pragma unroll
