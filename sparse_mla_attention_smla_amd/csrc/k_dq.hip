@@ -19,6 +19,8 @@
 // tile c (c < ceil(topk/32)), a [2H][32] bf16 block at ((t*ceil(topk/32) + c)*2H)*32:
 // rows 0..H-1 hold scale*dS of head h, rows H..2H-1 hold P, column j is the
 // j-th slot of the tile; tail columns past the last valid slot hold zeros.
+#include <type_traits>
+
 #include "kv_tile.hpp"
 #include "smla_launch.hpp"
 
@@ -32,7 +34,6 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
     static_assert(kNBuf == 4, "the vmcnt bounds below assume a 4-deep ring");
     constexpr int R = kBK / NW;   // DMA copies per wave per tile
-    constexpr int S = 4;          // dS/P stores per wave per tile
     __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
     __shared__ SlotList L;
 
@@ -72,8 +73,8 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     // one unrolled block that interleaves the dq MFMAs of tile j with the S/dP
     // MFMAs of tile j+1: two independent MFMA chains hide each other's LDS read
     // latency.  Tile j+3 is copied into the ring slot tile j-1 used.
-    // VMEM ops per wave: R copies per tile, 4 dS/P stores per tile; the vmcnt
-    // bound when waiting for tile j+1 counts the ops issued after its copies.
+    // VMEM ops per wave: R copies per tile and the dS/P stores; the vmcnt bound
+    // when waiting for tile j+1 counts only the copies issued after its own.
     int ctg = 0;  // compacted tiles of earlier chunks
     for (int k0 = 0; k0 < K; k0 += kChunk) {
         if (k0 > 0 && w == 0) compact_slots(idx_row, K, N, k0, &L, lane);
@@ -124,9 +125,11 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                              pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
             };
             for (int j = 0; j + 1 < ntile; ++j) {
-                if (j == 0) wait_vmcnt<(R < 63 ? R : 63)>();
-                else if (j == 1) wait_vmcnt<(R + S < 63 ? R + S : 63)>();
-                else wait_vmcnt<(R + 2 * S < 63 ? R + 2 * S : 63)>();
+                // Only the copies of tile j+2 are younger loads than those of tile
+                // j+1.  The dS/P stores in between are not counted: a store may
+                // retire before an older load, so an allowance for stores could
+                // let the wait pass early.  Over-waiting on them is safe.
+                wait_vmcnt<(R < 63 ? R : 63)>();
                 __syncthreads();  // tile j+1 landed everywhere; ring slot of tile j-1 is free
                 issue_tile<NW>(rsrc, &L, j + kNBuf - 1, ring + ((j + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
                 const u32x4 bf = softmax_grad(j);
@@ -168,179 +171,308 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     }
 }
 
-// Producer/consumer variant for 64-head groups (H % 64 == 0): 8 waves, two per
-// SIMD, so one wave's LDS and barrier waits are covered by the other's MFMAs.
-//   producers (waves 0-3): 16 heads each; q and dO in registers; S^T, dP^T of
-//     a tile, then P and scale*dS (stored as dsp blocks) and the dS fragment,
-//     published in LDS;
-//   consumers (waves 4-7): all 64 heads x 128 d of the dq accumulator each;
-//     every transposed kv read feeds four MFMAs (one per head group), which
-//     halves the LDS instructions of the dq product.
-// Waves w and w+4 share a SIMD (measured on gfx950 from HW_ID), so each SIMD
-// runs one producer and one consumer.
-// Producers run one tile ahead of consumers; one barrier per tile orders the
-// kv ring, the dS fragments (double-buffered) and the ring slot reuse.
-__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
-void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-                   const uint16_t* __restrict__ dO, const float* __restrict__ lse,
-                   const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
-                   int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
-    static_assert(kNBuf == 4, "the vmcnt bounds below assume a 4-deep ring");
-    constexpr int NWAVES = 8;
-    constexpr int R = kBK / NWAVES;   // copies per wave per tile
-    constexpr int S = 4;              // dS/P stores per producer per tile
-    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
-    __shared__ SlotList L;
-    __shared__ u32x4 dsfrag[2][4][64];  // dS fragments: [slot parity][producer][lane]
+// Items of one persistent workgroup: item ids lo, lo + step, ... below hi.
+// With a grid that is a multiple of 8, workgroup b runs on XCD b % 8 (blocks
+// are dealt to the XCDs in turn); each XCD then takes one contiguous eighth of
+// the items, so the tokens in flight on one XCD are neighbours and share their
+// kv rows in that XCD's L2.
+struct ItemSeq {
+    int lo, step, hi;
+    __device__ ItemSeq(int b, int G, int n_items) {
+        if ((G & 7) == 0 && n_items >= G) {
+            const int x = b & 7, G8 = G >> 3;
+            lo = (int)((long long)x * n_items / 8) + (b >> 3);
+            hi = (int)((long long)(x + 1) * n_items / 8);
+            step = G8;
+        } else {
+            lo = b;
+            hi = n_items;
+            step = G;
+        }
+    }
+    __device__ int count() const { return lo < hi ? (hi - lo + step - 1) / step : 0; }
+    __device__ int item(int r) const { return lo + r * step; }
+};
 
+// Persistent producer/consumer variant for 64-head groups (H % 64 == 0): one
+// 512-thread workgroup per CU walks its items (token, 64 heads); an item is cut
+// into segments of up to 512 index slots.  Waves w and w+4 share a SIMD
+// (measured on gfx950 from HW_ID), so each SIMD runs one wave of each role:
+//   producers (waves 0-3): 16 heads each, q and dO in registers; per tile the
+//     S^T, dP^T products, then P and scale*dS (stored as dsp blocks) and the dS
+//     fragment, published in LDS;
+//   consumers (waves 4-7): all 64 heads x 128 d of the dq accumulator each
+//     (every transposed kv read feeds four MFMAs); they also issue every kv
+//     row copy, so all explicit vmcnt waits count copies only.
+// Producers run one tile ahead of consumers; one barrier per tile.  The tiles
+// of consecutive segments form one stream over the 4-deep ring: while segment
+// s ends, the first tiles of segment s+1 are already copied, its slot list
+// (double-buffered, built by wave 4 during segment s) is ready, its first tile
+// is produced, and for a new item the producers reload q and dO during their
+// last tile of the old one.  Segments shorter than kMinStream tiles end with a
+// drain and restart instead.
+// Both roles run the same segment/tile control flow (same barrier sequence);
+// each role is its own instantiation so that only its state occupies registers.
+struct DqShared {
+    char* tiles;        // kNBuf ring slots of kTileBytes
+    SlotList* Lb;       // [2] slot lists, segment s uses Lb[s & 1]
+    u32x4 (*dsfrag)[4][64];  // [2][4][64] dS fragments: [position parity][producer][lane]
+};
+
+constexpr int kMinStream = 5;  // segments this long hand over to the next without a drain
+
+template <bool PROD>
+__device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                                           const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                                           const float* __restrict__ delta, const int32_t* __restrict__ idx,
+                                           int T, int H, int N, int K, float scale, uint16_t* __restrict__ dq,
+                                           uint16_t* __restrict__ dsp, const DqShared sh, int w, int lane) {
+    constexpr int R = kBK / 4;   // copies per consumer wave per tile
+    const int c16 = lane & 15, g = lane >> 4;
     const int nhg = H / 64;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int t = logical / nhg;
-    const int hg = logical - t * nhg;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-    const int32_t* idx_row = idx + (size_t)t * K;
-    // a consumer wave compacts the slots while the producers load q and dO
-    if (w == 4) compact_slots(idx_row, K, N, 0, &L, lane);
-    const i32x4 rsrc = make_rsrc(kv, (uint32_t)N * (kD * 2));
-    const uint32_t ring = lds_addr(tiles);
+    const ItemSeq seq(blockIdx.x, gridDim.x, T * nhg);
+    const int spi = (K + kChunk - 1) / kChunk;   // segments per item
+    const int nseg = seq.count() * spi;
+    if (nseg == 0) return;  // uniform: the whole workgroup has no item
     const int ntk = (K + kBK - 1) / kBK;
+    const uint32_t ring = lds_addr(sh.tiles);
+    SlotList* const Lb = sh.Lb;
+    auto seg_item = [&](int s) { return seq.item(s / spi); };
+    auto seg_k0 = [&](int s) { return (s % spi) * kChunk; };
 
-    if (w < 4) {
-        // ------------------------------------------------------------ producer
-        const int h = hg * 64 + w * 16 + c16;
-        const size_t qrow = ((size_t)t * H + h) * kD;
-        u32x4 qf[16], dof[16];
+    // ---------------------------------------------------------------- producer
+    u32x4 qf[16], dof[16];
+    float bias = 0.f, dl = 0.f;     // of the item being produced
+    float nbias = 0.f, ndl = 0.f;   // of the next item, loaded with its q/dO
+    int p_n = 0;                    // valid slots of the segment being produced
+    int p_ctg = 0;                  // compacted tiles of the item before that segment
+    int p_h = 0;                    // head of this lane
+    uint16_t* p_blk = dsp;          // dsp block of the item's compacted tile 0
+    const float c = scale * kLog2e;
+    auto item_rows = [&](int item, int& h, size_t& lrow) {
+        const int t = item / nhg, hg = item - t * nhg;
+        h = hg * 64 + w * 16 + c16;
+        lrow = (size_t)t * H + h;
+    };
+    auto bias_of = [](float l) { return (l == -INFINITY) ? INFINITY : l * kLog2e; };
+    auto load_item = [&](int item) {
+        int h; size_t lrow;
+        item_rows(item, h, lrow);
+        const size_t qrow = lrow * kD;
 #pragma unroll
         for (int ds = 0; ds < 16; ++ds) {
             qf[ds] = *reinterpret_cast<const u32x4*>(q + qrow + 32 * ds + 8 * g);
             dof[ds] = *reinterpret_cast<const u32x4*>(dO + qrow + 32 * ds + 8 * g);
         }
-        const float lse_h = lse[(size_t)t * H + h];
-        const float bias = (lse_h == -INFINITY) ? INFINITY : lse_h * kLog2e;
-        const float c = scale * kLog2e;
-        const float dl = delta[(size_t)t * H + h];
+        nbias = bias_of(lse[lrow]);
+        ndl = delta[lrow];
+    };
+    // point the producer at segment s (its slot list must be visible)
+    auto enter_segment = [&](int s, bool new_item) {
+        const int item = seg_item(s);
+        size_t lrow;
+        item_rows(item, p_h, lrow);
+        if (new_item) { bias = nbias; dl = ndl; p_ctg = 0; }
+        p_n = Lb[s & 1].n;
+        p_blk = dsp + (size_t)(item / nhg) * ntk * (2 * H) * kBK;
+    };
+    // S^T, dP^T of tile jt of the producer's segment (ring position pos) -> P,
+    // scale*dS (stored) -> dS fragment into LDS.  With RELOAD, each d-chunk of
+    // q/dO is replaced by the next item's right after its MFMAs.
+    auto produce = [&](int pos, int jt, auto reload, const uint16_t* nq, const uint16_t* nd) {
+        const char* buf = sh.tiles + (pos & (kNBuf - 1)) * kTileBytes;
         const int rb = rows_base(c16, g);
-        uint16_t* dsp_tok = dsp + (size_t)t * ntk * (2 * H) * kBK;
-        int ctg = 0;
-        for (int k0 = 0; k0 < K; k0 += kChunk) {
-            __syncthreads();
-            const int n = L.n;
-            const int ntile = (n + kBK - 1) / kBK;
+        f32x4 sacc[2], pacc[2];
 #pragma unroll
-            for (int p = 0; p < kNBuf - 1; ++p)
-                issue_tile<NWAVES>(rsrc, &L, p, ring + p * kTileBytes, w, lane);
-            // S^T, dP^T of tile j -> P, scale*dS (stored) -> dS fragment into LDS
-            auto produce = [&](int j) {
-                const char* buf = tiles + (j % kNBuf) * kTileBytes;
-                // four independent accumulation chains (S and dP of both 16-slot halves)
-                f32x4 sacc[2], pacc[2];
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int ds = 0; ds < 16; ++ds) {
-#pragma unroll
-                    for (int st = 0; st < 2; ++st) {
-                        const u32x4 a = tile_rows_a(buf, rb, st, ds);
-                        sacc[st] = mfma16(a, qf[ds], sacc[st]);
-                        pacc[st] = mfma16(a, dof[ds], pacc[st]);
-                    }
-                }
-                float dss[2][4], ps[2][4];
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool v = j * kBK + 16 * st + 4 * g + i < n;
-                        const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[st][i], c, -bias)) : 0.f;
-                        ps[st][i] = p;
-                        dss[st][i] = p * (pacc[st][i] - dl) * scale;
-                    }
-                uint16_t* blk = dsp_tok + (size_t)(ctg + j) * (2 * H) * kBK;
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    *reinterpret_cast<u32x2*>(blk + (size_t)h * kBK + 16 * st + 4 * g) =
-                        u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])};
-                    *reinterpret_cast<u32x2*>(blk + (size_t)(H + h) * kBK + 16 * st + 4 * g) =
-                        u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])};
-                }
-                dsfrag[j & 1][w][lane] =
-                    u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
-                          pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
-            };
-            if (ntile > 0) {
-                wait_vmcnt<2 * R>();
-                __syncthreads();
-                produce(0);
-                for (int j = 0; j < ntile; ++j) {
-                    if (j + 1 < ntile) {
-                        if (j == 0) wait_vmcnt<R + S>();
-                        else wait_vmcnt<R + 2 * S>();
-                    }
-                    __syncthreads();
-                    issue_tile<NWAVES>(rsrc, &L, j + kNBuf - 1,
-                                       ring + ((j + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
-                    if (j + 1 < ntile) produce(j + 1);
-                }
-            }
-            ctg += ntile;
-            wait_vmcnt<0>();
-            __syncthreads();
+        for (int st = 0; st < 2; ++st) {
+            sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
+            pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    } else {
-        // ------------------------------------------------------------ consumer
-        const int dq4 = w - 4;  // d in [128 dq4, 128 dq4 + 128)
-        const int cb = cols_base(c16, g);
-        f32x4 acc[8][4];
+#pragma unroll
+        for (int ds = 0; ds < 16; ++ds) {
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const u32x4 a = tile_rows_a(buf, rb, st, ds);
+                sacc[st] = mfma16(a, qf[ds], sacc[st]);
+                pacc[st] = mfma16(a, dof[ds], pacc[st]);
+            }
+            if constexpr (decltype(reload)::value) {
+                qf[ds] = *reinterpret_cast<const u32x4*>(nq + 32 * ds + 8 * g);
+                dof[ds] = *reinterpret_cast<const u32x4*>(nd + 32 * ds + 8 * g);
+            }
+        }
+        float dss[2][4], ps[2][4];
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool v = jt * kBK + 16 * st + 4 * g + i < p_n;
+                const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[st][i], c, -bias)) : 0.f;
+                ps[st][i] = p;
+                dss[st][i] = p * (pacc[st][i] - dl) * scale;
+            }
+        uint16_t* blk = p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK;
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+            *reinterpret_cast<u32x2*>(blk + (size_t)p_h * kBK + 16 * st + 4 * g) =
+                u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])};
+            *reinterpret_cast<u32x2*>(blk + (size_t)(H + p_h) * kBK + 16 * st + 4 * g) =
+                u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])};
+        }
+        sh.dsfrag[pos & 1][w][lane] =
+            u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
+                  pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
+    };
+    using NoReload = std::integral_constant<bool, false>;
+    using Reload = std::integral_constant<bool, true>;
+
+    // ---------------------------------------------------------------- consumer
+    const int dq4 = w - 4;  // d in [128 dq4, 128 dq4 + 128)
+    const i32x4 rsrc = make_rsrc(kv, (uint32_t)N * (kD * 2));
+    f32x4 acc[8][4];
+    if constexpr (!PROD) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < K; k0 += kChunk) {
-            if (k0 > 0 && w == 4) compact_slots(idx_row, K, N, k0, &L, lane);
-            __syncthreads();
-            const int n = L.n;
-            const int ntile = (n + kBK - 1) / kBK;
+    }
+    // consumer wave dq4 copies rows dq4, dq4 + 4, ... of tile ct of a slot list
+    auto issue = [&](const SlotList* L, int ct, int pos) {
+        issue_tile<4>(rsrc, L, ct, ring + (pos & (kNBuf - 1)) * kTileBytes, dq4, lane);
+    };
+    auto consume = [&](int pos) {
+        const int cb = cols_base(c16, g);
+        u32x4 b[4];
 #pragma unroll
-            for (int p = 0; p < kNBuf - 1; ++p)
-                issue_tile<NWAVES>(rsrc, &L, p, ring + p * kTileBytes, w, lane);
-            if (ntile > 0) {
-                wait_vmcnt<2 * R>();
-                __syncthreads();
-                for (int j = 0; j < ntile; ++j) {
-                    if (j + 1 < ntile) wait_vmcnt<R>();
-                    __syncthreads();
-                    issue_tile<NWAVES>(rsrc, &L, j + kNBuf - 1,
-                                       ring + ((j + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
-                    u32x4 b[4];
+        for (int m = 0; m < 4; ++m) b[m] = sh.dsfrag[pos & 1][m][lane];
+        const char* buf = sh.tiles + (pos & (kNBuf - 1)) * kTileBytes;
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) b[m] = dsfrag[j & 1][m][lane];
-                    const char* buf = tiles + (j % kNBuf) * kTileBytes;
+        for (int dt = 0; dt < 8; ++dt) {
+            const u32x4 a = tile_cols_a(buf, cb, 8 * dq4 + dt);
 #pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) {
-                        const u32x4 a = tile_cols_a(buf, cb, 8 * dq4 + dt);
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) acc[dt][m] = mfma16(a, b[m], acc[dt][m]);
-                    }
-                }
-            }
-            wait_vmcnt<0>();
-            __syncthreads();
+            for (int m = 0; m < 4; ++m) acc[dt][m] = mfma16(a, b[m], acc[dt][m]);
         }
-        // lane holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16
+    };
+    // lane holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16
+    auto epilogue = [&](int item) {
+        const int t = item / nhg, hg = item - t * nhg;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int h = hg * 64 + 16 * m + c16;
             uint16_t* out = dq + ((size_t)t * H + h) * kD + 128 * dq4 + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
+            for (int dt = 0; dt < 8; ++dt) {
                 *reinterpret_cast<u32x2*>(out + 16 * dt) =
                     u32x2{pack_bf16(acc[dt][m][0], acc[dt][m][1]), pack_bf16(acc[dt][m][2], acc[dt][m][3])};
+                acc[dt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
+    };
+
+    // ---------------------------------------------------------------- prologue
+    if constexpr (PROD) {
+        load_item(seg_item(0));
+    } else {
+        if (w == 4) compact_slots(idx + (size_t)(seg_item(0) / nhg) * K, K, N, seg_k0(0), &Lb[0], lane);
     }
+    __syncthreads();
+
+    SlotChunk nxt;     // wave 4: index slots of the next segment, loaded early
+    int base = 0;      // stream position of tile 0 of segment s
+    bool primed = false;
+    for (int s = 0; s < nseg; ++s) {
+        const int n = Lb[s & 1].n;
+        const int ntile = (n + kBK - 1) / kBK;
+        const bool first_of_item = (s % spi) == 0;
+        const bool last_of_item = (s % spi) == spi - 1;
+        const bool has_next = s + 1 < nseg;
+        const bool next_new_item = has_next && last_of_item;
+        const bool cont = has_next && ntile >= kMinStream;
+        const int item = seg_item(s);
+        const int32_t* idx_next = has_next ? idx + (size_t)(seg_item(s + 1) / nhg) * K : idx;
+        const int k0_next = has_next ? seg_k0(s + 1) : 0;
+        if (!primed) {
+            // restart: copy tiles 0..2 of s, then produce tile 0
+            if constexpr (PROD) {
+                enter_segment(s, first_of_item);
+            } else {
+#pragma unroll
+                for (int p = 0; p < kNBuf - 1; ++p) issue(&Lb[s & 1], p, base + p);
+                wait_vmcnt<2 * R>();
+            }
+            __syncthreads();
+            if constexpr (PROD) {
+                if (ntile > 0) produce(base, 0, NoReload{}, nullptr, nullptr);
+            }
+        }
+        for (int j = 0; j < ntile; ++j) {
+            const int pos = base + j;
+            if constexpr (!PROD) {
+                // tile pos+1 is produced in this iteration unless the stream ends;
+                // the only younger loads than its copies are those of tile pos+2
+                if (j + 1 < ntile || cont) wait_vmcnt<R>();
+            }
+            __syncthreads();
+            if constexpr (PROD) {
+                if (j + 1 < ntile) {
+                    if (j + 2 == ntile && cont && next_new_item) {
+                        int h; size_t lrow;
+                        item_rows(seg_item(s + 1), h, lrow);
+                        produce(pos + 1, j + 1, Reload{}, q + lrow * kD, dO + lrow * kD);
+                        nbias = bias_of(lse[lrow]);
+                        ndl = delta[lrow];
+                    } else {
+                        produce(pos + 1, j + 1, NoReload{}, nullptr, nullptr);
+                    }
+                } else if (cont) {
+                    if (!next_new_item) p_ctg += ntile;
+                    enter_segment(s + 1, next_new_item);
+                    if (p_n > 0) produce(pos + 1, 0, NoReload{}, nullptr, nullptr);
+                }
+            } else {
+                if (w == 4 && has_next && ntile >= 2 && j == 1)
+                    build_slot_list(nxt, N, k0_next, &Lb[(s + 1) & 1], lane);
+                const int ahead = j + kNBuf - 1;
+                if (ahead < ntile || !cont) issue(&Lb[s & 1], ahead, pos + kNBuf - 1);
+                else issue(&Lb[(s + 1) & 1], ahead - ntile, pos + kNBuf - 1);
+                consume(pos);
+                if (j + 1 == ntile && last_of_item) epilogue(item);
+                if (w == 4 && has_next && ntile >= 2 && j == 0) load_slot_chunk(idx_next, K, k0_next, nxt, lane);
+            }
+        }
+        if (!cont) {
+            // drain, then restart with segment s+1
+            if constexpr (PROD) {
+                if (next_new_item) load_item(seg_item(s + 1));
+                else if (has_next) p_ctg += ntile;
+            } else {
+                if (w == 4 && has_next && ntile < 2) compact_slots(idx_next, K, N, k0_next, &Lb[(s + 1) & 1], lane);
+                if (ntile == 0 && last_of_item) epilogue(item);
+                wait_vmcnt<0>();
+            }
+            __syncthreads();
+            primed = false;
+        } else {
+            primed = true;
+        }
+        base += ntile;
+    }
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                   const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                   const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
+                   int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
+    static_assert(kNBuf == 4, "the stream assumes a 4-deep ring");
+    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    const DqShared sh{tiles, Lb, dsfrag};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4) dq_pc_role<true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
+    else dq_pc_role<false>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
 }
 
 // Heads per workgroup: 64, 32 or 16 (whichever divides H first).
@@ -355,12 +487,19 @@ hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, 
                      uint16_t* dq, uint16_t* dsp, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int nw = dq_waves(H);
-    const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
-    switch (nw) {
-        case 4: smla_k2_dq_pc<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp); break;
-        case 2: smla_k2_dq<2><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp); break;
-        default: smla_k2_dq<1><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp); break;
+    if (nw == 4) {
+        // persistent: one workgroup per compute unit (its LDS use admits one)
+        const int items = T * (H / 64);
+        int cus = 0;
+        const hipError_t e = compute_units(&cus);
+        if (e != hipSuccess) return e;
+        const unsigned blocks = (unsigned)(items < cus ? items : cus);
+        smla_k2_dq_pc<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
+        return hipGetLastError();
     }
+    const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
+    if (nw == 2) smla_k2_dq<2><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
+    else smla_k2_dq<1><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
     return hipGetLastError();
 }
 

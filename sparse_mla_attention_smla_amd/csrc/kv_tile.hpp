@@ -80,30 +80,44 @@ struct SlotList {
     int32_t n;              // valid entries
 };
 
-// Compact the valid slots of [k0, min(k0 + kChunk, K)) of one index row.
-// Run by one wave (64 lanes); the caller synchronises afterwards.
-__device__ __forceinline__ void compact_slots(const int32_t* __restrict__ idx_row, int K, int N, int k0,
-                                              SlotList* L, int lane) {
+// Compaction of the valid slots of [k0, min(k0 + kChunk, K)) of one index row,
+// in two steps so the index loads can be issued well before the list is built.
+// Run by one wave (64 lanes); the caller synchronises before others read L.
+struct SlotChunk {
     int v[kChunk / 64];
+};
+
+__device__ __forceinline__ void load_slot_chunk(const int32_t* __restrict__ idx_row, int K, int k0,
+                                                SlotChunk& c, int lane) {
 #pragma unroll
     for (int s = 0; s < kChunk / 64; ++s) {
         const int k = k0 + 64 * s + lane;
-        v[s] = k < K ? idx_row[k] : -1;
+        c.v[s] = k < K ? idx_row[k] : -1;
     }
+}
+
+__device__ __forceinline__ void build_slot_list(const SlotChunk& c, int N, int k0, SlotList* L, int lane) {
     int base = 0;
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int s = 0; s < kChunk / 64; ++s) {
-        const bool ok = valid_row(v[s], N);
+        const bool ok = valid_row(c.v[s], N);
         const uint64_t m = __ballot(ok);
         if (ok) {
             const int p = base + __popcll(m & below);
             L->slot[p] = k0 + 64 * s + lane;
-            L->row[p] = v[s];
+            L->row[p] = c.v[s];
         }
         base += __popcll(m);
     }
     if (lane == 0) L->n = base;
+}
+
+__device__ __forceinline__ void compact_slots(const int32_t* __restrict__ idx_row, int K, int N, int k0,
+                                              SlotList* L, int lane) {
+    SlotChunk c;
+    load_slot_chunk(idx_row, K, k0, c, lane);
+    build_slot_list(c, N, k0, L, lane);
 }
 
 // Issue the buffer->LDS copies of tile `ct` (compacted positions 32ct..32ct+31)

@@ -37,6 +37,29 @@ smla_status check_arch() {
     return g_arch_state[dev] == 1 ? SMLA_OK : SMLA_ERR_ARCH;
 }
 
+}  // namespace
+
+// Compute units of the current device (cached per device).
+hipError_t smla::compute_units(int* n) {
+    static int cache[kMaxDevices] = {};
+    static std::mutex mu;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(mu);
+    if (cache[dev] == 0) {
+        int v = 0;
+        e = hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        cache[dev] = v > 0 ? v : 1;
+    }
+    *n = cache[dev];
+    return hipSuccess;
+}
+
+namespace {
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 struct Range {

@@ -8,6 +8,9 @@
 
 namespace smla {
 
+// Compute units of the current device (cached per device).
+hipError_t compute_units(int* n);
+
 // ---- streaming ------------------------------------------------------------
 hipError_t launch_delta(const uint16_t* o, const uint16_t* dO, int64_t rows, float* delta,
                         hipStream_t s);
