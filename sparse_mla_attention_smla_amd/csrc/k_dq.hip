@@ -171,27 +171,31 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     }
 }
 
-// Items of one persistent workgroup: item ids lo, lo + step, ... below hi.
-// With a grid that is a multiple of 8, workgroup b runs on XCD b % 8 (blocks
-// are dealt to the XCDs in turn); each XCD then takes one contiguous eighth of
-// the items, so the tokens in flight on one XCD are neighbours and share their
-// kv rows in that XCD's L2.
+// Items of one persistent workgroup: ids lo + r * G below n_items, r < count.
+// The items are dealt in rounds of G consecutive ids.  With a grid that is a
+// multiple of 8, workgroup b runs on XCD b % 8 (blocks are dealt to the XCDs
+// in turn) and gets id (b % 8) * G/8 + b / 8 of every round: each XCD works on
+// neighbouring items (their tokens share kv rows in that XCD's L2), and every
+// XCD sees every part of the token range (balanced work).  Workgroups start
+// their round sequence at different points (eight per XCD and four groups
+// within an XCD), so they do not all switch items, and reload q/dO from HBM,
+// at the same moment.
 struct ItemSeq {
-    int lo, step, hi;
+    int lo, step, n, r0;
     __device__ ItemSeq(int b, int G, int n_items) {
-        if ((G & 7) == 0 && n_items >= G) {
-            const int x = b & 7, G8 = G >> 3;
-            lo = (int)((long long)x * n_items / 8) + (b >> 3);
-            hi = (int)((long long)(x + 1) * n_items / 8);
-            step = G8;
-        } else {
-            lo = b;
-            hi = n_items;
-            step = G;
-        }
+        const bool xcd = (G & 7) == 0;
+        lo = xcd ? (b & 7) * (G >> 3) + (b >> 3) : b;
+        step = G;
+        n = lo < n_items ? (n_items - lo + G - 1) / G : 0;
+        const int phase = xcd ? (b & 7) * 4 + ((b >> 3) * 4) / (G >> 3) : 0;  // 0..31
+        r0 = (int)((long long)phase * n / 32);
     }
-    __device__ int count() const { return lo < hi ? (hi - lo + step - 1) / step : 0; }
-    __device__ int item(int r) const { return lo + r * step; }
+    __device__ int count() const { return n; }
+    __device__ int item(int r) const {
+        int rr = r + r0;
+        if (rr >= n) rr -= n;
+        return lo + rr * step;
+    }
 };
 
 // Persistent producer/consumer variant for 64-head groups (H % 64 == 0): one
@@ -217,9 +221,49 @@ struct DqShared {
     char* tiles;        // kNBuf ring slots of kTileBytes
     SlotList* Lb;       // [2] slot lists, segment s uses Lb[s & 1]
     u32x4 (*dsfrag)[4][64];  // [2][4][64] dS fragments: [position parity][producer][lane]
+    char* touch;             // 1 KiB landing area of the cache-warming copies (never read)
 };
 
 constexpr int kMinStream = 5;  // segments this long hand over to the next without a drain
+
+// q/dO B fragments.  In the MFMA B layout lane c16 + 16g holds head c16,
+// d-chunk g, so the four lanes of a quad name four different rows and the L1
+// splits each load into four times as many partial-line accesses (measured on
+// gfx950: about 15 B/clk per CU, from L2 too).  The fragments are therefore
+// loaded with lane 4*c16 + g holding head c16, chunk g (each quad reads 64
+// contiguous bytes of one row: about 50 B/clk) and moved to lane c16 + 16g
+// with one fixed lane permutation per register.  Reading the registers there
+// also makes the compiler complete their loads at that point: registers still
+// in flight at a loop's back edge would make it wait, with a vmcnt that also
+// covers every earlier store, at the start of each later iteration.
+__device__ __forceinline__ int frag_load_lane_row(int lane) { return lane >> 2; }
+__device__ __forceinline__ int frag_load_lane_chunk(int lane) { return lane & 3; }
+
+template <int N>
+__device__ __forceinline__ void frag_to_mfma_lanes(u32x4 (&r)[N], int lane) {
+    // destination lane l = c16 + 16g takes source lane 4*c16 + g
+    const int addr = 4 * (4 * (lane & 15) + (lane >> 4));
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            r[i][e] = (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)r[i][e]);
+}
+
+// Store side of the same effect: an MFMA accumulator or fragment lane c16 + 16g
+// holds 8 bytes of row c16 at chunk g, and a store in that lane order puts
+// four rows in every quad (measured on gfx950: 8 B/clk per CU against 30 for
+// quad-contiguous rows).  This moves the value to lane 4*c16 + g, so each quad
+// stores one row's 32 contiguous bytes; the store address must follow.
+__device__ __forceinline__ u32x2 to_quad_rows(u32x2 v, int lane) {
+    const int addr = 4 * ((lane >> 2) + 16 * (lane & 3));   // source lane c16 + 16g of lane 4*c16 + g
+    return u32x2{(uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v[0]),
+                 (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v[1])};
+}
+
+__device__ __forceinline__ void settle_scalars(float a, float b) {
+    asm volatile("" : : "v"(a), "v"(b));
+}
 
 template <bool PROD>
 __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
@@ -228,6 +272,8 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                                            int T, int H, int N, int K, float scale, uint16_t* __restrict__ dq,
                                            uint16_t* __restrict__ dsp, const DqShared sh, int w, int lane) {
     constexpr int R = kBK / 4;   // copies per consumer wave per tile
+    constexpr int kEpiStores = 32;  // global stores of one consumer epilogue (4 heads x 8 d-blocks)
+    constexpr int kWarmTiles = 8;   // tiles over which the next item's q/dO are warmed (32 chunks)
     const int c16 = lane & 15, g = lane >> 4;
     const int nhg = H / 64;
     const ItemSeq seq(blockIdx.x, gridDim.x, T * nhg);
@@ -255,17 +301,28 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         lrow = (size_t)t * H + h;
     };
     auto bias_of = [](float l) { return (l == -INFINITY) ? INFINITY : l * kLog2e; };
+    // first element of this lane's load row (lane 4*c16 + g: head c16, chunk g)
+    auto frag_src = [&](int item) {
+        const int t = item / nhg, hg = item - t * nhg;
+        return ((size_t)t * H + hg * 64 + w * 16 + frag_load_lane_row(lane)) * kD +
+               8 * frag_load_lane_chunk(lane);
+    };
     auto load_item = [&](int item) {
         int h; size_t lrow;
         item_rows(item, h, lrow);
-        const size_t qrow = lrow * kD;
+        const size_t src = frag_src(item);
 #pragma unroll
         for (int ds = 0; ds < 16; ++ds) {
-            qf[ds] = *reinterpret_cast<const u32x4*>(q + qrow + 32 * ds + 8 * g);
-            dof[ds] = *reinterpret_cast<const u32x4*>(dO + qrow + 32 * ds + 8 * g);
+            qf[ds] = *reinterpret_cast<const u32x4*>(q + src + 32 * ds);
+            dof[ds] = *reinterpret_cast<const u32x4*>(dO + src + 32 * ds);
         }
         nbias = bias_of(lse[lrow]);
         ndl = delta[lrow];
+    };
+    auto finish_load = [&]() {
+        frag_to_mfma_lanes(qf, lane);
+        frag_to_mfma_lanes(dof, lane);
+        settle_scalars(nbias, ndl);
     };
     // point the producer at segment s (its slot list must be visible)
     auto enter_segment = [&](int s, bool new_item) {
@@ -297,8 +354,8 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 pacc[st] = mfma16(a, dof[ds], pacc[st]);
             }
             if constexpr (decltype(reload)::value) {
-                qf[ds] = *reinterpret_cast<const u32x4*>(nq + 32 * ds + 8 * g);
-                dof[ds] = *reinterpret_cast<const u32x4*>(nd + 32 * ds + 8 * g);
+                qf[ds] = *reinterpret_cast<const u32x4*>(nq + 32 * ds);
+                dof[ds] = *reinterpret_cast<const u32x4*>(nd + 32 * ds);
             }
         }
         float dss[2][4], ps[2][4];
@@ -311,13 +368,16 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 ps[st][i] = p;
                 dss[st][i] = p * (pacc[st][i] - dl) * scale;
             }
-        uint16_t* blk = p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK;
+        // dsp rows of this wave's 16 heads, quad-contiguous: lane 4*c + g stores
+        // head (p_h - c16 + c), columns 16st + 4g .. +3
+        uint16_t* blk = p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK +
+                        (size_t)(p_h - c16 + (lane >> 2)) * kBK + 4 * (lane & 3);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            *reinterpret_cast<u32x2*>(blk + (size_t)p_h * kBK + 16 * st + 4 * g) =
-                u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])};
-            *reinterpret_cast<u32x2*>(blk + (size_t)(H + p_h) * kBK + 16 * st + 4 * g) =
-                u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])};
+            *reinterpret_cast<u32x2*>(blk + 16 * st) = to_quad_rows(
+                u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])}, lane);
+            *reinterpret_cast<u32x2*>(blk + (size_t)H * kBK + 16 * st) = to_quad_rows(
+                u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])}, lane);
         }
         sh.dsfrag[pos & 1][w][lane] =
             u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
@@ -340,6 +400,19 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     auto issue = [&](const SlotList* L, int ct, int pos) {
         issue_tile<4>(rsrc, L, ct, ring + (pos & (kNBuf - 1)) * kTileBytes, dq4, lane);
     };
+    // Cache warming: during a segment's last tiles the consumers read the next
+    // item's q and dO rows (64 KiB each, in 4 KiB chunks of 64 lines) into a
+    // scratch LDS area, so that the producers' reload of them hits L2/MALL.
+    // Every iteration issues exactly one such copy per consumer (a zero-length
+    // one when there is nothing to warm), which keeps the vmcnt bounds exact.
+    const uint32_t touch_lds = lds_addr(sh.touch);
+    auto touch = [&](int item_next, int k) {
+        const bool real = item_next >= 0 && k >= 0 && k < 32;
+        const int it = real ? item_next : 0;
+        const int t = it / nhg, hg = it - t * nhg;
+        const uint16_t* rows = (k < 16 ? q : dO) + ((size_t)t * H + hg * 64) * kD;
+        copy_row_to_lds(make_rsrc(rows, real ? 65536u : 0u), touch_lds, (k & 15) * 4096 + lane * 64);
+    };
     auto consume = [&](int pos) {
         const int cb = cols_base(c16, g);
         u32x4 b[4];
@@ -353,17 +426,18 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             for (int m = 0; m < 4; ++m) acc[dt][m] = mfma16(a, b[m], acc[dt][m]);
         }
     };
-    // lane holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16
+    // lane c16 + 16g holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16;
+    // stored quad-contiguous (lane 4*c + g writes head 16m + c)
     auto epilogue = [&](int item) {
         const int t = item / nhg, hg = item - t * nhg;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const int h = hg * 64 + 16 * m + c16;
-            uint16_t* out = dq + ((size_t)t * H + h) * kD + 128 * dq4 + 4 * g;
+            const int h = hg * 64 + 16 * m + (lane >> 2);
+            uint16_t* out = dq + ((size_t)t * H + h) * kD + 128 * dq4 + 4 * (lane & 3);
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                *reinterpret_cast<u32x2*>(out + 16 * dt) =
-                    u32x2{pack_bf16(acc[dt][m][0], acc[dt][m][1]), pack_bf16(acc[dt][m][2], acc[dt][m][3])};
+                *reinterpret_cast<u32x2*>(out + 16 * dt) = to_quad_rows(
+                    u32x2{pack_bf16(acc[dt][m][0], acc[dt][m][1]), pack_bf16(acc[dt][m][2], acc[dt][m][3])}, lane);
                 acc[dt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -372,6 +446,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     // ---------------------------------------------------------------- prologue
     if constexpr (PROD) {
         load_item(seg_item(0));
+        finish_load();
     } else {
         if (w == 4) compact_slots(idx + (size_t)(seg_item(0) / nhg) * K, K, N, seg_k0(0), &Lb[0], lane);
     }
@@ -380,6 +455,8 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     SlotChunk nxt;     // wave 4: index slots of the next segment, loaded early
     int base = 0;      // stream position of tile 0 of segment s
     bool primed = false;
+    int post_epi = 0;  // consumer: iterations whose wait must skip the last epilogue's stores
+    int since = 0;     // consumer: iterations since the last restart
     for (int s = 0; s < nseg; ++s) {
         const int n = Lb[s & 1].n;
         const int ntile = (n + kBK - 1) / kBK;
@@ -399,6 +476,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
 #pragma unroll
                 for (int p = 0; p < kNBuf - 1; ++p) issue(&Lb[s & 1], p, base + p);
                 wait_vmcnt<2 * R>();
+                since = 0;
             }
             __syncthreads();
             if constexpr (PROD) {
@@ -408,19 +486,36 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         for (int j = 0; j < ntile; ++j) {
             const int pos = base + j;
             if constexpr (!PROD) {
-                // tile pos+1 is produced in this iteration unless the stream ends;
-                // the only younger loads than its copies are those of tile pos+2
-                if (j + 1 < ntile || cont) wait_vmcnt<R>();
+                // Tile pos+1 is produced in this iteration unless the stream ends.
+                // Vector memory ops complete in issue order, so the bound is the
+                // count of ops issued after its copies: tile pos+2's copies, the
+                // warming copies of the last two iterations (one each, none before
+                // a restart), and the dq stores of an epilogue run in one of the
+                // last two iterations.
+                if (j + 1 < ntile || cont) {
+                    if (post_epi > 0) {
+                        if (since == 0) wait_vmcnt<R + kEpiStores>();
+                        else if (since == 1) wait_vmcnt<R + 1 + kEpiStores>();
+                        else wait_vmcnt<R + 2 + kEpiStores>();
+                    } else {
+                        if (since == 0) wait_vmcnt<R>();
+                        else if (since == 1) wait_vmcnt<R + 1>();
+                        else wait_vmcnt<R + 2>();
+                    }
+                }
             }
             __syncthreads();
             if constexpr (PROD) {
                 if (j + 1 < ntile) {
                     if (j + 2 == ntile && cont && next_new_item) {
                         int h; size_t lrow;
-                        item_rows(seg_item(s + 1), h, lrow);
-                        produce(pos + 1, j + 1, Reload{}, q + lrow * kD, dO + lrow * kD);
+                        const int nitem = seg_item(s + 1);
+                        item_rows(nitem, h, lrow);
+                        const size_t src = frag_src(nitem);
+                        produce(pos + 1, j + 1, Reload{}, q + src, dO + src);
                         nbias = bias_of(lse[lrow]);
                         ndl = delta[lrow];
+                        finish_load();
                     } else {
                         produce(pos + 1, j + 1, NoReload{}, nullptr, nullptr);
                     }
@@ -435,20 +530,35 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 const int ahead = j + kNBuf - 1;
                 if (ahead < ntile || !cont) issue(&Lb[s & 1], ahead, pos + kNBuf - 1);
                 else issue(&Lb[(s + 1) & 1], ahead - ntile, pos + kNBuf - 1);
+                {
+                    const int first = ntile > kWarmTiles + 2 ? ntile - kWarmTiles - 2 : 0;
+                    const bool warm = next_new_item && j >= first && j + 2 < ntile;
+                    touch(warm ? seg_item(s + 1) : -1, (j - first) * 4 + dq4);
+                }
                 consume(pos);
-                if (j + 1 == ntile && last_of_item) epilogue(item);
+                if (post_epi > 0) --post_epi;
+                ++since;
+                if (j + 1 == ntile && last_of_item) {
+                    epilogue(item);
+                    post_epi = 2;
+                }
                 if (w == 4 && has_next && ntile >= 2 && j == 0) load_slot_chunk(idx_next, K, k0_next, nxt, lane);
             }
         }
         if (!cont) {
             // drain, then restart with segment s+1
             if constexpr (PROD) {
-                if (next_new_item) load_item(seg_item(s + 1));
-                else if (has_next) p_ctg += ntile;
+                if (next_new_item) {
+                    load_item(seg_item(s + 1));
+                    finish_load();
+                } else if (has_next) {
+                    p_ctg += ntile;
+                }
             } else {
                 if (w == 4 && has_next && ntile < 2) compact_slots(idx_next, K, N, k0_next, &Lb[(s + 1) & 1], lane);
                 if (ntile == 0 && last_of_item) epilogue(item);
                 wait_vmcnt<0>();
+                post_epi = 0;
             }
             __syncthreads();
             primed = false;
@@ -468,7 +578,8 @@ void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
     __shared__ SlotList Lb[2];
     __shared__ u32x4 dsfrag[2][4][64];
-    const DqShared sh{tiles, Lb, dsfrag};
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    const DqShared sh{tiles, Lb, dsfrag, touch};
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (w < 4) dq_pc_role<true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
