@@ -130,9 +130,12 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             const char* ybuf = smem + (it % kYRing) * kYBytes;
 #pragma unroll
             for (int sst = 0; sst < 2; ++sst) {
-                const int pos = it * kBK + 16 * sst + c16;
+                // lane c16 + 16g computes slot it*32 + 16sst + c16, columns
+                // 64w + 16dt + 4g .. +3; the rows are stored quad-contiguous:
+                // lane 4c + g writes slot it*32 + 16sst + c
+                const int pos = it * kBK + 16 * sst + (lane >> 2);
                 const int slot = pos < n ? L.slot[pos] : 0;
-                uint16_t* orow = interm + ((size_t)t * K + slot) * kD + 64 * w + 4 * g;
+                uint16_t* orow = interm + ((size_t)t * K + slot) * kD + 64 * w + 4 * (lane & 3);
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
                     f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
@@ -143,10 +146,9 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                         const u32x2 hi = ds_read_tr16(p + 16 * kYPitch);
                         cacc = mfma16(xf[dt][ks], u32x4{lo[0], lo[1], hi[0], hi[1]}, cacc);
                     }
-                    if (pos < n) {
-                        const u32x2 v = {pack_bf16(cacc[0], cacc[1]), pack_bf16(cacc[2], cacc[3])};
-                        *reinterpret_cast<u32x2*>(orow + 16 * dt) = v;
-                    }
+                    const u32x2 v = to_quad_rows(
+                        u32x2{pack_bf16(cacc[0], cacc[1]), pack_bf16(cacc[2], cacc[3])}, lane);
+                    if (pos < n) *reinterpret_cast<u32x2*>(orow + 16 * dt) = v;
                 }
             }
             if (more) store_tile(smem + ((it + 1) % kYRing) * kYBytes);

@@ -56,4 +56,16 @@ __device__ __forceinline__ T wave_xor(T v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+
+// An MFMA accumulator or fragment lane c16 + 16g holds 8 bytes of row c16 at
+// chunk g, so a store in that lane order puts four rows in every quad of
+// lanes (measured on gfx950: 8 B/clk per CU, against 30 for quad-contiguous
+// rows).  to_quad_rows moves the value to lane 4*c16 + g, so each quad stores
+// one row's 32 contiguous bytes; the caller's store address must follow.
+__device__ __forceinline__ u32x2 to_quad_rows(u32x2 v, int lane) {
+    const int addr = 4 * ((lane >> 2) + 16 * (lane & 3));   // source lane c16 + 16g of lane 4*c16 + g
+    return u32x2{(uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v[0]),
+                 (uint32_t)__builtin_amdgcn_ds_bpermute(addr, (int)v[1])};
+}
+
 }  // namespace smla
