@@ -81,21 +81,26 @@ __global__ __launch_bounds__(128) void smla_k6_dsink_partial(const float* __rest
     partial[(int64_t)blockIdx.x * H + h] = acc;
 }
 
-__global__ __launch_bounds__(128) void smla_k6_dsink_final(const float* __restrict__ partial,
+// One wave per head: lane l sums partials l, l + 64, ... in order, then a
+// butterfly in a fixed pattern combines the lanes (same result every run).
+__global__ __launch_bounds__(256) void smla_k6_dsink_final(const float* __restrict__ partial,
                                                            int nblocks, int H,
                                                            float* __restrict__ d_sink) {
-    const int h = threadIdx.x;
-    if (h >= H) return;
+    const int h = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (h >= H) return;  // whole wave: H is a multiple of 16, the grid covers ceil(H / 4)
     float acc = 0.f;
-    for (int b = 0; b < nblocks; ++b) acc += partial[(int64_t)b * H + h];
-    d_sink[h] = 0.f - acc;
+    for (int b = lane; b < nblocks; b += 64) acc += partial[(int64_t)b * H + h];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += wave_xor(acc, m);
+    if (lane == 0) d_sink[h] = 0.f - acc;
 }
 
 hipError_t launch_dsink(const float* lse, const float* delta, const float* sink, int T, int H,
                         float* partial, float* d_sink, hipStream_t s) {
     const int nb = dsink_blocks(T);
     if (nb > 0) smla_k6_dsink_partial<<<nb, 128, 0, s>>>(lse, delta, sink, T, H, partial);
-    smla_k6_dsink_final<<<1, 128, 0, s>>>(partial, nb, H, d_sink);
+    smla_k6_dsink_final<<<(H + 3) / 4, 256, 0, s>>>(partial, nb, H, d_sink);
     return hipGetLastError();
 }
 
