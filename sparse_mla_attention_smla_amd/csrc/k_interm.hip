@@ -130,24 +130,30 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             const char* ybuf = smem + (it % kYRing) * kYBytes;
 #pragma unroll
             for (int sst = 0; sst < 2; ++sst) {
-                // lane c16 + 16g computes slot it*32 + 16sst + c16, columns
-                // 64w + 16dt + 4g .. +3; the rows are stored quad-contiguous:
-                // lane 4c + g writes slot it*32 + 16sst + c
+                // every B fragment (32 r x 16 slots) is read once and feeds the four
+                // d-blocks of this wave (four accumulation chains)
+                f32x4 cacc[4];
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) cacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const char* p = ybuf + yb + ks * 32 * kYPitch + sst * 32;
+                    const u32x2 lo = ds_read_tr16(p);
+                    const u32x2 hi = ds_read_tr16(p + 16 * kYPitch);
+                    const u32x4 bfrag = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt) cacc[dt] = mfma16(xf[dt][ks], bfrag, cacc[dt]);
+                }
+                // lane c16 + 16g holds slot it*32 + 16sst + c16, columns 64w + 16dt + 4g
+                // .. +3; the rows are stored quad-contiguous: lane 4c + g writes slot
+                // it*32 + 16sst + c
                 const int pos = it * kBK + 16 * sst + (lane >> 2);
                 const int slot = pos < n ? L.slot[pos] : 0;
                 uint16_t* orow = interm + ((size_t)t * K + slot) * kD + 64 * w + 4 * (lane & 3);
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    f32x4 cacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) {
-                        const char* p = ybuf + yb + ks * 32 * kYPitch + sst * 32;
-                        const u32x2 lo = ds_read_tr16(p);
-                        const u32x2 hi = ds_read_tr16(p + 16 * kYPitch);
-                        cacc = mfma16(xf[dt][ks], u32x4{lo[0], lo[1], hi[0], hi[1]}, cacc);
-                    }
                     const u32x2 v = to_quad_rows(
-                        u32x2{pack_bf16(cacc[0], cacc[1]), pack_bf16(cacc[2], cacc[3])}, lane);
+                        u32x2{pack_bf16(cacc[dt][0], cacc[dt][1]), pack_bf16(cacc[dt][2], cacc[dt][3])}, lane);
                     if (pos < n) *reinterpret_cast<u32x2*>(orow + 16 * dt) = v;
                 }
             }
