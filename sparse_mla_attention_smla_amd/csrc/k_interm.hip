@@ -42,7 +42,9 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     constexpr int kYChunks = R * kBK * 2 / 16;           // 16-B chunks of one dsp block
     constexpr int kYPT = (kYChunks + kIThreads - 1) / kIThreads;
     static_assert(kYRing * kYBytes <= kStageBytes, "Y ring must fit in the staging area");
-    __shared__ __attribute__((aligned(16))) char smem[kStageBytes];
+    constexpr int kPasses = (R + kStageRows - 1) / kStageRows;
+    constexpr int kRowsPerWave = kStageRows / kIWaves;   // row copies per wave per pass
+    __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];  // two staging buffers
     __shared__ SlotList L;
 
     const int t = blockIdx.x;
@@ -51,6 +53,27 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;
     const size_t tok = (size_t)t * H * kD;
     const int32_t* idx_row = idx + (size_t)t * K;
+
+    // ---- X = [q_t; dO_t] (R rows of 1 KiB) is copied straight into LDS, one
+    // row per buffer->LDS copy, in passes of 64 rows through two staging
+    // buffers: pass p+2 is in flight while pass p is read into registers.
+    // Rows past R (a short last pass) read out of range and land as zeros.
+    const i32x4 rq = make_rsrc(q + tok, (uint32_t)H * kD * 2);
+    const i32x4 rd = make_rsrc(dO + tok, (uint32_t)H * kD * 2);
+    const uint32_t stage0 = lds_addr(smem);
+    auto issue_pass = [&](int p) {
+        const uint32_t buf = stage0 + (p & 1) * kStageBytes;
+#pragma unroll
+        for (int i = 0; i < kRowsPerWave; ++i) {
+            const int r = w + kIWaves * i;          // staged row within the pass
+            const int row = p * kStageRows + r;     // X row
+            const bool is_q = row < H;
+            const int off = row < R ? (is_q ? row : row - H) * (kD * 2) + (lane << 4) : (1 << 30);
+            copy_row_to_lds(is_q ? rq : rd, buf + r * kRowPitch, off);
+        }
+    };
+    issue_pass(0);
+    if (kPasses > 1) issue_pass(1);
     if (w == 0) compact_slots(idx_row, K, N, 0, &L, lane);
 
     // ---- X^T fragments: xf[dt][ks] holds column 64w + 16dt + c16 of X rows
@@ -60,33 +83,27 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // odd-multiple-of-32 pitch is free of LDS bank conflicts.
     u32x4 xf[4][NKS];
     const int xb = (4 * g + (c16 >> 2)) * kRowPitch + (64 * w + 4 * (c16 & 3)) * 2;
-    for (int c0 = 0; c0 < R; c0 += kStageRows) {
 #pragma unroll
-        for (int i = 0; i < kStageRows * (kD / 8) / kIThreads; ++i) {
-            const int id = tid + kIThreads * i;
-            const int r = id >> 6, ch = id & 63;
-            const int row = c0 + r;
-            if (row < R) {
-                const uint16_t* src = row < H ? q + tok + (size_t)row * kD
-                                              : dO + tok + (size_t)(row - H) * kD;
-                *reinterpret_cast<u32x4*>(smem + r * kRowPitch + ch * 16) =
-                    *reinterpret_cast<const u32x4*>(src + ch * 8);
-            }
-        }
+    for (int p = 0; p < kPasses; ++p) {
+        // this wave's copies of pass p are done once only pass p+1's are younger
+        if (p + 1 < kPasses) wait_vmcnt<kRowsPerWave>();
+        else wait_vmcnt<0>();
         __syncthreads();
+        const char* sbuf = smem + (p & 1) * kStageBytes;
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
-            if (32 * ks >= c0 && 32 * ks < c0 + kStageRows) {
-                const char* p = smem + xb + (32 * ks - c0) * kRowPitch;
+            if (32 * ks >= p * kStageRows && 32 * ks < (p + 1) * kStageRows) {
+                const char* ptr = sbuf + xb + (32 * ks - p * kStageRows) * kRowPitch;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
-                    const u32x2 lo = ds_read_tr16(p + dt * 32);
-                    const u32x2 hi = ds_read_tr16(p + 16 * kRowPitch + dt * 32);
+                    const u32x2 lo = ds_read_tr16(ptr + dt * 32);
+                    const u32x2 hi = ds_read_tr16(ptr + 16 * kRowPitch + dt * 32);
                     xf[dt][ks] = u32x4{lo[0], lo[1], hi[0], hi[1]};
                 }
             }
         }
         __syncthreads();
+        if (p + 2 < kPasses) issue_pass(p + 2);
     }
 
     // ---- stream the Y tiles (one dsp block per compacted tile)
@@ -113,6 +130,12 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
     };
 
+    // Output rows go out as buffer stores: the slot list decides the row, and a
+    // lane whose position is past the last valid slot gets an offset past the
+    // token's range, which the hardware drops.  Every store is issued by every
+    // wave, so the compiler can count them when it waits for the Y prefetch.
+    const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        interm + (size_t)t * K * kD, (short)0, K * kD * 2, 0x00020000);
     int ctg = 0;
     for (int k0 = 0; k0 < K; k0 += kChunk) {
         if (k0 > 0 && w == 0) compact_slots(idx_row, K, N, k0, &L, lane);
@@ -122,11 +145,17 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         if (ntile > 0) {
             load_tile(ctg);
             store_tile(smem);
+            if (ntile > 1) load_tile(ctg + 1);
         }
         __syncthreads();
         for (int it = 0; it < ntile; ++it) {
-            const bool more = it + 1 < ntile;
-            if (more) load_tile(ctg + it + 1);
+            // tile it+1 (loaded during the previous iteration) goes to the ring slot
+            // that tile it-1 used; its loads are older than the previous
+            // iteration's stores, so waiting for them does not wait for those
+            if (it + 1 < ntile) {
+                store_tile(smem + ((it + 1) % kYRing) * kYBytes);
+                if (it + 2 < ntile) load_tile(ctg + it + 2);
+            }
             const char* ybuf = smem + (it % kYRing) * kYBytes;
 #pragma unroll
             for (int sst = 0; sst < 2; ++sst) {
@@ -148,16 +177,14 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 // .. +3; the rows are stored quad-contiguous: lane 4c + g writes slot
                 // it*32 + 16sst + c
                 const int pos = it * kBK + 16 * sst + (lane >> 2);
-                const int slot = pos < n ? L.slot[pos] : 0;
-                uint16_t* orow = interm + ((size_t)t * K + slot) * kD + 64 * w + 4 * (lane & 3);
+                const int voff = pos < n ? (L.slot[pos] * kD + 64 * w + 4 * (lane & 3)) * 2 : K * kD * 2;
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) {
                     const u32x2 v = to_quad_rows(
                         u32x2{pack_bf16(cacc[dt][0], cacc[dt][1]), pack_bf16(cacc[dt][2], cacc[dt][3])}, lane);
-                    if (pos < n) *reinterpret_cast<u32x2*>(orow + 16 * dt) = v;
+                    __builtin_amdgcn_raw_buffer_store_b64(v, out_rsrc, voff + 32 * dt, 0, 0);
                 }
             }
-            if (more) store_tile(smem + ((it + 1) % kYRing) * kYBytes);
             __syncthreads();
         }
         ctg += ntile;
