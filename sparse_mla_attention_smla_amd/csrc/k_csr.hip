@@ -78,23 +78,59 @@ __global__ __launch_bounds__(kSortThreads) void smla_k4_csr_sort(const int32_t* 
         for (int i = 0; i < kSortThreads / 64; ++i) s += wsum[i];
         inv[b] = s;
     }
-    // bitonic sorting network, ascending
+    // Bitonic sorting network, ascending.  Thread T holds keys 8T .. 8T+7 in
+    // registers; for partner distance j < 8 the exchange is inside the thread,
+    // for 8 <= j < 512 it is with lane T ^ (j/8) of the same wave (a shuffle),
+    // and only the six stages with j >= 512 go through LDS.
+    static_assert(kCsrBlock == 8 * kSortThreads, "eight keys per thread");
+    __syncthreads();
+    uint32_t v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = keys[8 * tid + e];
+    __syncthreads();
     for (int k = 2; k <= kCsrBlock; k <<= 1) {
         for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < kCsrBlock; i += kSortThreads) {
-                const int ixj = i ^ j;
-                if (ixj > i) {
-                    const uint32_t a = keys[i], c = keys[ixj];
+            if (j >= 512) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) keys[8 * tid + e] = v[e];
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = 8 * tid + e;
+                    const uint32_t o = keys[i ^ j];
                     const bool up = (i & k) == 0;
-                    if ((a > c) == up) {
-                        keys[i] = c;
-                        keys[ixj] = a;
+                    const bool lower = (i & j) == 0;   // i < i ^ j
+                    v[e] = (lower == up) ? min(v[e], o) : max(v[e], o);
+                }
+                __syncthreads();
+            } else if (j >= 8) {
+                const int lm = j >> 3;                  // partner lane distance
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int i = 8 * tid + e;
+                    const uint32_t o = (uint32_t)__shfl_xor((int)v[e], lm, 64);
+                    const bool up = (i & k) == 0;
+                    const bool lower = (i & j) == 0;
+                    v[e] = (lower == up) ? min(v[e], o) : max(v[e], o);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int pe = e ^ j;
+                    if (pe > e) {
+                        const int i = 8 * tid + e;
+                        const bool up = (i & k) == 0;
+                        const uint32_t a = v[e], c = v[pe];
+                        v[e] = up ? min(a, c) : max(a, c);
+                        v[pe] = up ? max(a, c) : min(a, c);
                     }
                 }
             }
-            __syncthreads();
         }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) keys[8 * tid + e] = v[e];
+    __syncthreads();
     const int nloc = (int)min((int64_t)kCsrBlock, M - base);
     for (int p = tid; p < nloc; p += kSortThreads) sorted[base + p] = keys[p];
     int32_t* crow = cnt + (int64_t)b * N;
