@@ -133,10 +133,17 @@ __global__ __launch_bounds__(kSortThreads) void smla_k4_csr_sort(const int32_t* 
     __syncthreads();
     const int nloc = (int)min((int64_t)kCsrBlock, M - base);
     for (int p = tid; p < nloc; p += kSortThreads) sorted[base + p] = keys[p];
+    // Per-row counts: thread T takes rows [j0, j1), finds the first key of row
+    // j0 by binary search and walks the sorted keys from there (invalid slots
+    // and the sentinel sort after every valid row).
     int32_t* crow = cnt + (int64_t)b * N;
-    for (int j = tid; j < N; j += kSortThreads) {
-        crow[j] = lower_bound_row(keys, kCsrBlock, (uint32_t)j + 1) -
-                  lower_bound_row(keys, kCsrBlock, (uint32_t)j);
+    const int rpt = (N + kSortThreads - 1) / kSortThreads;
+    const int j0 = min(N, tid * rpt), j1 = min(N, j0 + rpt);
+    int p = lower_bound_row(keys, kCsrBlock, (uint32_t)j0);
+    for (int j = j0; j < j1; ++j) {
+        int c = 0;
+        while (p < kCsrBlock && (keys[p] >> 12) == (uint32_t)j) { ++p; ++c; }
+        crow[j] = c;
     }
 }
 
