@@ -334,14 +334,28 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
             pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
+        // kv fragments are read two d-chunks ahead of their MFMAs (the schedule
+        // is pinned: the compiler's own keeps about one chunk ahead)
+        constexpr int PF = 2;
+        u32x4 ab[16][2];
+#pragma unroll
+        for (int ds = 0; ds < PF; ++ds)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) ab[ds][st] = tile_rows_a(buf, rb, st, ds);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
 #pragma unroll
         for (int ds = 0; ds < 16; ++ds) {
+            if (ds + PF < 16) {
+#pragma unroll
+                for (int st = 0; st < 2; ++st) ab[ds + PF][st] = tile_rows_a(buf, rb, st, ds + PF);
+            }
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
-                const u32x4 a = tile_rows_a(buf, rb, st, ds);
-                sacc[st] = mfma16(a, qf[ds], sacc[st]);
-                pacc[st] = mfma16(a, dof[ds], pacc[st]);
+                sacc[st] = mfma16(ab[ds][st], qf[ds], sacc[st]);
+                pacc[st] = mfma16(ab[ds][st], dof[ds], pacc[st]);
             }
+            if (ds + PF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
             if constexpr (decltype(reload)::value) {
                 qf[ds] = *reinterpret_cast<const u32x4*>(nq + 32 * ds);
                 dof[ds] = *reinterpret_cast<const u32x4*>(nd + 32 * ds);
@@ -408,11 +422,18 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
 #pragma unroll
         for (int m = 0; m < 4; ++m) b[m] = sh.dsfrag[pos & 1][m][lane];
         const char* buf = sh.tiles + (pos & (kNBuf - 1)) * kTileBytes;
+        // transposed kv reads two d-blocks ahead of their four MFMAs (pinned)
+        u32x4 ca[8];
+        ca[0] = tile_cols_a(buf, cb, 8 * dq4);
+        ca[1] = tile_cols_a(buf, cb, 8 * dq4 + 1);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 + 4, 0);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-            const u32x4 a = tile_cols_a(buf, cb, 8 * dq4 + dt);
+            if (dt + 2 < 8) ca[dt + 2] = tile_cols_a(buf, cb, 8 * dq4 + dt + 2);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) acc[dt][m] = mfma16(a, b[m], acc[dt][m]);
+            for (int m = 0; m < 4; ++m) acc[dt][m] = mfma16(ca[dt], b[m], acc[dt][m]);
+            if (dt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
     };
     // lane c16 + 16g holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16;
