@@ -26,8 +26,14 @@
  *    ranges must not overlap any other argument (else SMLA_ERR_INVALID_ARG).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    work: they return without synchronising; results are ready when the
- *    stream reaches that point.  No hipMemset is enqueued (every output cell is
- *    written by a kernel), so calls may be captured into a HIP graph.
+ *    stream reaches that point.  smla_bwd also uses one library-owned helper
+ *    stream per device (default priority): it forks there with an event
+ *    recorded on `stream` and joins back with an event that `stream` waits
+ *    on, so all of its results are still ordered on `stream`.  No hipMemset is
+ *    enqueued (every output cell is written by a kernel), so calls may be
+ *    captured into a HIP graph (the fork/join is the usual captured pattern).
+ *    Concurrent smla_bwd calls from several host threads are safe; their
+ *    enqueues are serialised.
  *  - Argument errors are reported synchronously before anything is enqueued.
  *    SMLA_ERR_ARCH is returned when the current device is not gfx950 (the
  *    page's wrapper likewise refuses other architectures).  A failed launch

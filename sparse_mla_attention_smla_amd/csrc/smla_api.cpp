@@ -60,6 +60,31 @@ hipError_t smla::compute_units(int* n) {
 
 namespace {
 
+// A helper stream per device (default priority, non-blocking) with a fork and
+// a join event: smla_bwd runs the CSR build there, concurrently with delta,
+// dQ and the intermediate, and joins before the gather.  One mutex covers a
+// whole smla_bwd enqueue so calls from several host threads cannot interleave
+// records of the shared events.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    int state = 0;  // 0 not tried, 1 ready, 2 unavailable
+};
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+SideStream* side_stream(int dev) {
+    SideStream& d = g_side[dev];
+    if (d.state == 0) {
+        d.state = 2;
+        if (hipStreamCreateWithFlags(&d.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&d.join, hipEventDisableTiming) == hipSuccess)
+            d.state = 1;
+    }
+    return d.state == 1 ? &d : nullptr;
+}
+
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 struct Range {
@@ -230,14 +255,30 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
     const GatherScratch gs = gather_carve(ws + L.gather, M, num_kv);
     float* dsink_part = reinterpret_cast<float*>(ws + L.dsink);
 
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* side = side_stream(dev);
+    // The CSR depends only on the indices: it runs on the helper stream while
+    // delta, dQ and the intermediate run on the caller's (or first, in order,
+    // when no helper stream could be made).
+    if (side != nullptr) {
+        if (hipEventRecord(side->fork, s) != hipSuccess ||
+            hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+            return SMLA_ERR_HIP;
+        if (launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, side->s) != hipSuccess)
+            return SMLA_ERR_HIP;
+        if (hipEventRecord(side->join, side->s) != hipSuccess) return SMLA_ERR_HIP;
+    } else if (launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, s) != hipSuccess) {
+        return SMLA_ERR_HIP;
+    }
     hipError_t e;
-    // The CSR depends only on the indices; it goes first.
-    if ((e = launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, s)) != hipSuccess) return SMLA_ERR_HIP;
     if ((e = launch_delta(o, dO, (int64_t)T * H, delta, s)) != hipSuccess) return SMLA_ERR_HIP;
     if ((e = launch_dq(q, kv, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dsp, s)) != hipSuccess)
         return SMLA_ERR_HIP;
     if ((e = launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm, s)) != hipSuccess)
         return SMLA_ERR_HIP;
+    if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SMLA_ERR_HIP;
     if ((e = launch_gather(interm, row_ptr, slots, M, num_kv, gs, dkv, s)) != hipSuccess)
         return SMLA_ERR_HIP;
     if (sink != nullptr)

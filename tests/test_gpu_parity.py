@@ -181,6 +181,45 @@ def test_deterministic_and_poisoned_workspace(small_case):
         assert torch.equal(a[2], b[2]) and torch.equal(a[2], c[2])
 
 
+def test_graph_capture_replays_match_eager(small_case):
+    """smla_bwd (including its fork to the helper stream and the join back) is
+    captured into a graph; every replay, with eager work and synchronisations in
+    between, must equal the eager call bit for bit (the results are
+    deterministic, so equality is the right bar)."""
+    name, x, ref, d = small_case
+    T, H, _ = x["q"].shape
+    N, K = x["kv"].shape[0], x["idx"].shape[1]
+    ws = torch.empty((B.bwd_workspace_bytes(T, H, N, K),), dtype=torch.uint8, device="cuda")
+    eager = _run_bwd(d, workspace=ws)
+    dq = torch.empty_like(d["q"])
+    dkv = torch.empty_like(d["kv"])
+    ds = torch.empty_like(d["sink"]) if d["sink"] is not None else None
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm-up call on the capture stream, outside capture
+        B.smla_bwd(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"], SCALE,
+                   workspace=ws, out=(dq, dkv, ds))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.smla_bwd(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"], SCALE,
+                   workspace=ws, out=(dq, dkv, ds))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dq.fill_(0); dkv.fill_(0)       # eager work between replays
+        if ds is not None:
+            ds.fill_(0)
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(host_bits_t(dq), host_bits_t(eager[0])), f"replay {rep}: dq"
+        assert torch.equal(host_bits_t(dkv), host_bits_t(eager[1])), f"replay {rep}: dkv"
+        if ds is not None:
+            assert torch.equal(ds, eager[2]), f"replay {rep}: d_sink"
+
+
 # ---------------------------------------------------------------------------
 # forward (test-input producer)
 # ---------------------------------------------------------------------------
