@@ -157,15 +157,28 @@ GatherScratch gather_carve(void* base, int64_t M, int N) {
     return w;
 }
 
-hipError_t launch_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots,
-                         int64_t M, int N, const GatherScratch& ws, uint16_t* dkv, hipStream_t s) {
+hipError_t launch_gather_plan(const int32_t* row_ptr, int64_t M, int N, const GatherScratch& ws,
+                              hipStream_t s) {
     const int64_t ms = gather_max_segments(M, N);
     smla_k5_gather_plan<<<1, 1024, 0, s>>>(row_ptr, N, M, (int)ms, ws.seg_ptr, ws.seg_row);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_sum(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots,
+                             int64_t M, int N, const GatherScratch& ws, uint16_t* dkv, hipStream_t s) {
+    const int64_t ms = gather_max_segments(M, N);
     smla_k5_gather_segment<<<(unsigned)ms, kSegWaves * 64, 0, s>>>(interm, row_ptr, slots,
                                                                    ws.seg_ptr, ws.seg_row, N, M,
                                                                    ws.partial);
     smla_k5_gather_combine<<<(N + 3) / 4, 256, 0, s>>>(ws.partial, ws.seg_ptr, N, dkv);
     return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots,
+                         int64_t M, int N, const GatherScratch& ws, uint16_t* dkv, hipStream_t s) {
+    const hipError_t e = launch_gather_plan(row_ptr, M, N, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_gather_sum(interm, row_ptr, slots, M, N, ws, dkv, s);
 }
 
 }  // namespace smla

@@ -60,14 +60,15 @@ hipError_t smla::compute_units(int* n) {
 
 namespace {
 
-// A helper stream per device (default priority, non-blocking) with a fork and
-// a join event: smla_bwd runs the CSR build there, concurrently with delta,
-// dQ and the intermediate, and joins before the gather.  One mutex covers a
+// A helper stream per device (default priority, non-blocking) with fork, join
+// and after-delta events: smla_bwd runs the CSR build, the gather plan and
+// (once delta is done) d_sink there, concurrently with delta, dQ and the
+// intermediate, and joins before the gather sums.  One mutex covers a
 // whole smla_bwd enqueue so calls from several host threads cannot interleave
 // records of the shared events.
 struct SideStream {
     hipStream_t s = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr, after_delta = nullptr;
     int state = 0;  // 0 not tried, 1 ready, 2 unavailable
 };
 SideStream g_side[kMaxDevices];
@@ -79,7 +80,8 @@ SideStream* side_stream(int dev) {
         d.state = 2;
         if (hipStreamCreateWithFlags(&d.s, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&d.join, hipEventDisableTiming) == hipSuccess)
+            hipEventCreateWithFlags(&d.join, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&d.after_delta, hipEventDisableTiming) == hipSuccess)
             d.state = 1;
     }
     return d.state == 1 ? &d : nullptr;
@@ -259,31 +261,34 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
     if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_side_mu);
     SideStream* side = side_stream(dev);
-    // The CSR depends only on the indices: it runs on the helper stream while
-    // delta, dQ and the intermediate run on the caller's (or first, in order,
-    // when no helper stream could be made).
+    // The CSR and the gather plan depend only on the indices, d_sink only on
+    // lse and delta: they run on the helper stream while dQ and the
+    // intermediate run on the caller's stream (all in one order on the
+    // caller's stream when no helper stream could be made).
+    hipStream_t aux = side != nullptr ? side->s : s;
     if (side != nullptr) {
         if (hipEventRecord(side->fork, s) != hipSuccess ||
-            hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+            hipStreamWaitEvent(aux, side->fork, 0) != hipSuccess)
             return SMLA_ERR_HIP;
-        if (launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, side->s) != hipSuccess)
-            return SMLA_ERR_HIP;
-        if (hipEventRecord(side->join, side->s) != hipSuccess) return SMLA_ERR_HIP;
-    } else if (launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, s) != hipSuccess) {
-        return SMLA_ERR_HIP;
     }
-    hipError_t e;
-    if ((e = launch_delta(o, dO, (int64_t)T * H, delta, s)) != hipSuccess) return SMLA_ERR_HIP;
-    if ((e = launch_dq(q, kv, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dsp, s)) != hipSuccess)
+    if (launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, aux) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_gather_plan(row_ptr, M, num_kv, gs, aux) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_delta(o, dO, (int64_t)T * H, delta, s) != hipSuccess) return SMLA_ERR_HIP;
+    if (sink != nullptr) {
+        if (side != nullptr && (hipEventRecord(side->after_delta, s) != hipSuccess ||
+                                hipStreamWaitEvent(aux, side->after_delta, 0) != hipSuccess))
+            return SMLA_ERR_HIP;
+        if (launch_dsink(lse, delta, sink, T, H, dsink_part, d_sink, aux) != hipSuccess)
+            return SMLA_ERR_HIP;
+    }
+    if (side != nullptr && hipEventRecord(side->join, aux) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_dq(q, kv, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dsp, s) != hipSuccess)
         return SMLA_ERR_HIP;
-    if ((e = launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm, s)) != hipSuccess)
+    if (launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm, s) != hipSuccess)
         return SMLA_ERR_HIP;
     if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SMLA_ERR_HIP;
-    if ((e = launch_gather(interm, row_ptr, slots, M, num_kv, gs, dkv, s)) != hipSuccess)
+    if (launch_gather_sum(interm, row_ptr, slots, M, num_kv, gs, dkv, s) != hipSuccess)
         return SMLA_ERR_HIP;
-    if (sink != nullptr)
-        if ((e = launch_dsink(lse, delta, sink, T, H, dsink_part, d_sink, s)) != hipSuccess)
-            return SMLA_ERR_HIP;
     return SMLA_OK;
 }
 

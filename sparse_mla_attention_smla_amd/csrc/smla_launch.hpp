@@ -43,6 +43,12 @@ struct GatherScratch {
 };
 size_t gather_scratch_bytes(int64_t M, int N);
 GatherScratch gather_carve(void* base, int64_t M, int N);
+// plan (needs only row_ptr) and the sums (need the intermediate) can be
+// enqueued on different streams; launch_gather does both in order
+hipError_t launch_gather_plan(const int32_t* row_ptr, int64_t M, int N, const GatherScratch& ws,
+                              hipStream_t s);
+hipError_t launch_gather_sum(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots,
+                             int64_t M, int N, const GatherScratch& ws, uint16_t* dkv, hipStream_t s);
 hipError_t launch_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots,
                          int64_t M, int N, const GatherScratch& ws, uint16_t* dkv, hipStream_t s);
 
