@@ -24,8 +24,12 @@ design notes):
   * a row with no valid slot and no sink has lse = -inf and contributes zero
     everywhere (exp(-inf - (-inf)) is never evaluated);
   * duplicate indices within a row are independent slots;
-  * lse is a side output and is not differentiated (the API takes no dlse);
-  * d_sink[h] = -sum_t P_sink[t,h] * delta[t,h]  (dO/dsink = -P_sink * O);
+  * an optional upstream gradient of lse, dlse [T,H], is the one input the
+    page does not name.  Since d lse / d S_k = P_k and d lse / d sink = P_sink,
+    it adds P * dlse to dS and P_sink * dlse to d_sink; both terms are what
+    replacing delta by delta - dlse gives.  Without it, dlse = 0;
+  * d_sink[h] = -sum_t P_sink[t,h] * (delta[t,h] - dlse[t,h])
+    (dO/dsink = -P_sink * O, dlse/dsink = P_sink);
   * the CSR lists valid slots s = t*topk + k ordered by (index, s).
 """
 from __future__ import annotations
@@ -165,16 +169,16 @@ def emit_forward_outputs(O, lse):
 # --------------------------------------------------------------------------
 
 
-def backward_token(q_t, kv64, dO_t, O_t, lse_t, idx_row, sink64, scale):
+def backward_token(q_t, kv64, dO_t, O_t, lse_t, idx_row, sink64, scale, dlse_t=None):
     """Backward of one query token, all heads, following the phase definitions.
 
     delta = rowsum(O * dO)
     P     = exp(S - lse)        S = scale * q kv^T        (0 on masked slots)
     dP    = dO kv^T
-    dS    = P * (dP - delta)
+    dS    = P * (dP - delta + dlse)        (dlse = 0 when not given)
     dq    = scale * dS kv
     interm[k] = sum_h (scale * dS[h,k] q[h] + P[h,k] dO[h])   (0 on masked slots)
-    d_sink contribution = -P_sink * delta
+    d_sink contribution = -P_sink * (delta - dlse)
 
     Returns a dict of per-token arrays; P, dS are [H, K], interm is [K, D].
     """
@@ -183,10 +187,11 @@ def backward_token(q_t, kv64, dO_t, O_t, lse_t, idx_row, sink64, scale):
     v = _valid(idx_row, kv64.shape[0])
     G = kv64[idx_row[v]]
     delta = np.sum(O_t * dO_t, axis=1)
+    dl = np.zeros(H) if dlse_t is None else np.asarray(dlse_t, dtype=np.float64)
     s = scale * (q_t @ G.T)
     Pv = _probs(s, lse_t)
     dPv = dO_t @ G.T
-    dSv = Pv * (dPv - delta[:, None])
+    dSv = Pv * (dPv - delta[:, None] + dl[:, None])
     dq = scale * (dSv @ G) if G.shape[0] else np.zeros((H, Dh))
     P = np.zeros((H, K))
     dS = np.zeros((H, K))
@@ -196,12 +201,12 @@ def backward_token(q_t, kv64, dO_t, O_t, lse_t, idx_row, sink64, scale):
     interm[v] = scale * (dSv.T @ q_t) + Pv.T @ dO_t
     p_sink = _sink_prob(sink64, lse_t)
     return {"dq": dq, "delta": delta, "P": P, "dS": dS, "interm": interm,
-            "dsink": -p_sink * delta, "valid": v}
+            "dsink": -p_sink * (delta - dl), "valid": v}
 
 
-def backward(q, kv, dO, O, lse, idx, sink, scale, stages=False):
+def backward(q, kv, dO, O, lse, idx, sink, scale, stages=False, dlse=None):
     """Full backward in float64.  Inputs as consumed by the op: q, kv, dO, O as
-    bf16 bits (or floats), lse float, idx int, sink [H] or None.
+    bf16 bits (or floats), lse float, idx int, sink [H] or None, dlse [T,H] or None.
 
     Returns dict with dq [T,H,D], dkv [N,D], d_sink [H] (None without a sink),
     delta [T,H]; with stages=True also P, dS [T,H,K] and interm [T,K,D].
@@ -222,7 +227,8 @@ def backward(q, kv, dO, O, lse, idx, sink, scale, stages=False):
         interm = np.zeros((T, K, Dh))
     for t in range(T):
         row = np.asarray(idx[t])
-        r = backward_token(_as64(q[t]), kv64, _as64(dO[t]), _as64(O[t]), lse64[t], row, s64, scale)
+        r = backward_token(_as64(q[t]), kv64, _as64(dO[t]), _as64(O[t]), lse64[t], row, s64, scale,
+                           None if dlse is None else dlse[t])
         dq[t] = r["dq"]
         delta[t] = r["delta"]
         dsink += r["dsink"]
@@ -236,18 +242,19 @@ def backward(q, kv, dO, O, lse, idx, sink, scale, stages=False):
     return out
 
 
-def backward_tokens(q, kv, dO, O, lse, idx, sink, scale, tokens):
+def backward_tokens(q, kv, dO, O, lse, idx, sink, scale, tokens, dlse=None):
     """dq, delta, P, dS and interm for a subset of query tokens only."""
     kv64 = _as64(kv)
     H = np.shape(q)[1]
     s64 = _sink64(sink, H)
     lse64 = np.asarray(lse, dtype=np.float64)
     res = [backward_token(_as64(q[t]), kv64, _as64(dO[t]), _as64(O[t]), lse64[t],
-                          np.asarray(idx[t]), s64, scale) for t in tokens]
+                          np.asarray(idx[t]), s64, scale, None if dlse is None else dlse[t])
+           for t in tokens]
     return {k: np.stack([r[k] for r in res]) for k in ("dq", "delta", "P", "dS", "interm")}
 
 
-def dkv_rows(q, kv, dO, O, lse, idx, sink, scale, rows):
+def dkv_rows(q, kv, dO, O, lse, idx, sink, scale, rows, dlse=None):
     """dkv for selected kv rows only: the sum of interm over every valid slot
     (t, k) with idx[t, k] == j, each slot's interm evaluated from its definition."""
     kv64 = _as64(kv)
@@ -260,23 +267,26 @@ def dkv_rows(q, kv, dO, O, lse, idx, sink, scale, rows):
         for t in np.unique(ts):
             q_t, dO_t = _as64(q[t]), _as64(dO[t])
             delta = np.sum(_as64(O[t]) * dO_t, axis=1)
+            dl = 0.0 if dlse is None else np.asarray(dlse[t], dtype=np.float64)
             g = kv64[j]
             s = scale * (q_t @ g)
             P = _probs(s[:, None], lse64[t])[:, 0]
-            dS = P * (dO_t @ g - delta)
+            dS = P * (dO_t @ g - delta + dl)
             contrib = scale * (dS @ q_t) + P @ dO_t
             out[r] += contrib * np.count_nonzero(ts == t)
     return out
 
 
-def d_sink(dO, O, lse, sink):
-    """d_sink[h] = -sum_t exp(sink[h] - lse[t,h]) * rowsum(O * dO)[t,h]."""
+def d_sink(dO, O, lse, sink, dlse=None):
+    """d_sink[h] = -sum_t exp(sink[h] - lse[t,h]) * (rowsum(O * dO)[t,h] - dlse[t,h])."""
     T, H, _ = np.shape(O)
     s64 = _sink64(sink, H)
     lse64 = np.asarray(lse, dtype=np.float64)
     acc = np.zeros(H)
     for t in range(T):
         delta = np.sum(_as64(O[t]) * _as64(dO[t]), axis=1)
+        if dlse is not None:
+            delta = delta - np.asarray(dlse[t], dtype=np.float64)
         acc -= _sink_prob(s64, lse64[t]) * delta
     return acc
 

@@ -138,11 +138,79 @@ def test_random_direction_derivative_at_full_width():
 
 
 # --------------------------------------------------------------------------
+# with an upstream gradient of lse: L = <dO, O> + <dlse, lse>
+# --------------------------------------------------------------------------
+
+def _loss_lse(q, kv, sink, dO, dlse, idx, scale):
+    O, lse = orc.forward(q, kv, idx, sink, scale)
+    live = np.isfinite(lse)      # a row with no slot and no sink has lse = -inf, constant
+    return float(np.sum(O * dO) + np.sum(dlse[live] * lse[live]))
+
+
+@pytest.mark.parametrize("with_sink", [True, False])
+def test_dlse_backward_matches_central_differences(with_sink):
+    q, kv, dO, idx, sink, scale = _fd_case(8, with_sink, seed=31 + with_sink)
+    dlse = np.random.default_rng(41).standard_normal((q.shape[0], q.shape[1]))
+    O, lse = orc.forward(q, kv, idx, sink, scale)
+    g = orc.backward(q, kv, dO, O, lse, idx, sink, scale, dlse=dlse)
+
+    def fd(arr):
+        out = np.empty(arr.shape)
+        for i in np.ndindex(arr.shape):
+            x0 = arr[i]
+            eps = 1e-6 * max(1.0, abs(x0))
+            arr[i] = x0 + eps
+            lp = _loss_lse(q, kv, sink, dO, dlse, idx, scale)
+            arr[i] = x0 - eps
+            lm = _loss_lse(q, kv, sink, dO, dlse, idx, scale)
+            arr[i] = x0
+            out[i] = (lp - lm) / (2 * eps)
+        return out
+
+    np.testing.assert_allclose(g["dq"], fd(q), rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(g["dkv"], fd(kv), rtol=1e-6, atol=1e-8)
+    if with_sink:
+        np.testing.assert_allclose(g["d_sink"], fd(sink), rtol=1e-6, atol=1e-8)
+    assert np.all(g["dq"][3] == 0.0)
+
+
+def test_dlse_alone_closed_forms():
+    # dO = 0 and dlse = 1: the gradient of sum(lse).  d lse / d q = scale * sum_k P_k kv_k
+    # = scale * O (the forward's output), and d lse / d sink = P_sink.
+    q, kv, dO, idx, sink, scale = _random_case(7)
+    O, lse = orc.forward(q, kv, idx, sink, scale)
+    g = orc.backward(q, kv, np.zeros_like(dO), O, lse, idx, sink, scale, dlse=np.ones(lse.shape))
+    np.testing.assert_allclose(g["dq"], scale * O, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(g["d_sink"], np.exp(sink[None, :] - lse).sum(0), rtol=1e-12)
+
+
+def test_linearity_in_dO_and_dlse():
+    q, kv, dO, idx, sink, scale = _random_case(8)
+    rng = np.random.default_rng(98)
+    dO2 = rng.standard_normal(dO.shape)
+    O, lse = orc.forward(q, kv, idx, sink, scale)
+    d1, d2 = rng.standard_normal(lse.shape), rng.standard_normal(lse.shape)
+    a, b = 1.3, -0.6
+    g1 = orc.backward(q, kv, dO, O, lse, idx, sink, scale, dlse=d1)
+    g2 = orc.backward(q, kv, dO2, O, lse, idx, sink, scale, dlse=d2)
+    g12 = orc.backward(q, kv, a * dO + b * dO2, O, lse, idx, sink, scale, dlse=a * d1 + b * d2)
+    for k in ("dq", "dkv", "d_sink"):
+        np.testing.assert_allclose(g12[k], a * g1[k] + b * g2[k], rtol=1e-11, atol=1e-12)
+    toks = [1, 9]
+    s = orc.backward_tokens(q, kv, dO, O, lse, idx, sink, scale, toks, dlse=d1)
+    np.testing.assert_allclose(s["dq"], g1["dq"][toks], rtol=1e-14)
+    np.testing.assert_allclose(orc.dkv_rows(q, kv, dO, O, lse, idx, sink, scale, [0, 4], dlse=d1),
+                               g1["dkv"][[0, 4]], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(orc.d_sink(dO, O, lse, sink, dlse=d1), g1["d_sink"], rtol=1e-13)
+
+
+# --------------------------------------------------------------------------
 # dense special case == causal attention with a sink logit (torch, autograd)
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("with_dlse", [False, True])
 @pytest.mark.parametrize("with_sink", [True, False])
-def test_dense_causal_case_matches_torch_sdpa(with_sink):
+def test_dense_causal_case_matches_torch_sdpa(with_sink, with_dlse):
     from torch.nn.attention import SDPBackend, sdpa_kernel
     rng = np.random.default_rng(3)
     T, H, D = 12, 4, 32
@@ -155,8 +223,9 @@ def test_dense_causal_case_matches_torch_sdpa(with_sink):
     dO = rng.standard_normal((T, H, D))
     sink = rng.standard_normal(H)
 
+    dlse = rng.standard_normal((T, H)) if with_dlse else None
     O, lse = orc.forward(q, kv, idx, sink if with_sink else None, scale)
-    g = orc.backward(q, kv, dO, O, lse, idx, sink if with_sink else None, scale)
+    g = orc.backward(q, kv, dO, O, lse, idx, sink if with_sink else None, scale, dlse=dlse)
 
     tq = torch.tensor(q, requires_grad=True)
     tkv = torch.tensor(kv, requires_grad=True)
@@ -178,7 +247,10 @@ def test_dense_causal_case_matches_torch_sdpa(with_sink):
     ref_lse = torch.logsumexp(scale * (qh @ kh.transpose(-1, -2)) + mask[None], dim=-1)[0].T
     np.testing.assert_allclose(O, ref_O.detach().numpy(), rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(lse, ref_lse.detach().numpy(), rtol=1e-12, atol=1e-13)
-    ref_O.backward(torch.tensor(dO))
+    loss = torch.sum(ref_O * torch.tensor(dO))
+    if with_dlse:
+        loss = loss + torch.sum(ref_lse * torch.tensor(dlse))
+    loss.backward()
     np.testing.assert_allclose(g["dq"], tq.grad.numpy(), rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(g["dkv"], tkv.grad.numpy(), rtol=1e-10, atol=1e-12)
     if with_sink:
