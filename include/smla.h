@@ -98,6 +98,10 @@ size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk);
  * table (phases delta, dQ, dKV-interm, CSR build, dKV gather, d_sink).
  *   q, dO, o  bf16 [T, H, 512]   kv bf16 [num_kv, 512]   lse float [T, H]
  *   idx int32 [T, topk]          sink float [H] or NULL
+ *   dlse float [T, H] or NULL: upstream gradient of lse, for callers that use
+ *             lse downstream (the page's op takes none; NULL means zero).  It
+ *             must be finite.  Derived: d lse / d S_k = P_k and
+ *             d lse / d sink = P_sink, so it enters as delta -> delta - dlse.
  *   dq  bf16 [T, H, 512] out     dkv bf16 [num_kv, 512] out
  *   d_sink float [H] out; must be non-NULL exactly when sink is non-NULL
  *   n_invalid int32 [1] out or NULL: count of index values that are neither
@@ -105,13 +109,13 @@ size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk);
  *   workspace device scratch of at least smla_bwd_workspace_bytes() bytes,
  *             owned by the caller; its contents on entry do not matter.
  * Math (per token t, head h, valid slot k): P = exp(scale*<q,kv_k> - lse),
- * dP = <dO, kv_k>, delta = <O, dO>, dS = P*(dP - delta);
+ * dP = <dO, kv_k>, delta = <O, dO> - dlse, dS = P*(dP - delta);
  * dq = scale * sum_k dS kv_k;  dkv[j] = sum over slots (t,k) with idx = j of
  * sum_h (scale*dS q[t,h] + P dO[t,h]);  d_sink[h] = -sum_t exp(sink - lse)*delta.
  * Rows with lse = -inf contribute nothing.  dq/dkv accumulate in fp32.
  */
 int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
-             const float* lse, const int32_t* idx, const float* sink,
+             const float* lse, const int32_t* idx, const float* sink, const float* dlse,
              int T, int H, int num_kv, int topk, float scale,
              uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
              void* workspace, size_t workspace_bytes, void* stream);
@@ -121,11 +125,13 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
 /* ------------------------------------------------------------------------ */
 
 /*
- * smla_delta -- delta[t,h] = sum_d O[t,h,d] * dO[t,h,d] (bf16 in, fp32 accumulation).
+ * smla_delta -- delta[t,h] = sum_d O[t,h,d] * dO[t,h,d] (bf16 in, fp32 accumulation),
+ * minus dlse[t,h] when dlse is given (the shift smla_bwd applies for it).
  * Page: aiter PR 4766, Structure table, "delta = rowsum(O*dO)" row.
- *   o, dO bf16 [T, H, 512]   delta float [T, H] out
+ *   o, dO bf16 [T, H, 512]   dlse float [T, H] or NULL   delta float [T, H] out
  */
-int smla_delta(const uint16_t* o, const uint16_t* dO, int T, int H, float* delta, void* stream);
+int smla_delta(const uint16_t* o, const uint16_t* dO, const float* dlse, int T, int H,
+               float* delta, void* stream);
 
 /*
  * smla_dq -- dq and the per-slot probabilities/gradients of the logits.

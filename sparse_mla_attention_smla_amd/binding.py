@@ -33,8 +33,8 @@ _SIGNATURES = {
     "smla_status_string": ([_I], ctypes.c_char_p),
     "smla_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "smla_bwd_workspace_bytes": ([_I, _I, _I, _I], _Z),
-    "smla_bwd": ([_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
-    "smla_delta": ([_P, _P, _I, _I, _P, _P], _I),
+    "smla_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "smla_delta": ([_P, _P, _P, _I, _I, _P, _P], _I),
     "smla_dq": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "smla_interm": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "smla_csr_workspace_bytes": ([_I, _I, _I], _Z),
@@ -146,10 +146,11 @@ def bwd_workspace(T, H, num_kv, topk, device):
 
 
 def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=None,
-             count_invalid=False):
+             count_invalid=False, dlse=None):
     """Sparse MLA backward: returns (dq, dkv, d_sink[, n_invalid]).
 
     out, if given, is a tuple (dq, dkv, d_sink) of preallocated outputs.
+    dlse, if given, is the upstream gradient of lse (fp32 [T, H]).
     """
     T, H, _ = q.shape
     N, K = kv.shape[0], idx.shape[1]
@@ -161,6 +162,8 @@ def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=
     _need(idx, "idx", torch.int32, (T, K))
     if sink is not None:
         _need(sink, "sink", torch.float32, (H,))
+    if dlse is not None:
+        _need(dlse, "dlse", torch.float32, (T, H))
     if out is None:
         dq = torch.empty_like(q)
         dkv = torch.empty_like(kv)
@@ -171,7 +174,7 @@ def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=
         workspace = bwd_workspace(T, H, N, K, q.device)
     n_inv = torch.empty((1,), dtype=torch.int32, device=q.device) if count_invalid else None
     _check("smla_bwd", lib().smla_bwd(
-        _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), T, H, N, K,
+        _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
         _default_scale(scale), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
         _ptr(workspace), workspace.numel(), _stream(q.device)))
     if count_invalid:
@@ -183,13 +186,17 @@ def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=
 # stages
 # ---------------------------------------------------------------------------
 
-def smla_delta(o, dO, delta=None):
+def smla_delta(o, dO, delta=None, dlse=None):
+    """delta = rowsum(o * dO) (minus dlse when given), fp32 [T, H]."""
     T, H, _ = o.shape
     _need(o, "o", torch.bfloat16, (T, H, D))
     _need(dO, "dO", torch.bfloat16, (T, H, D))
+    if dlse is not None:
+        _need(dlse, "dlse", torch.float32, (T, H))
     if delta is None:
         delta = torch.empty((T, H), dtype=torch.float32, device=o.device)
-    _check("smla_delta", lib().smla_delta(_ptr(o), _ptr(dO), T, H, _ptr(delta), _stream(o.device)))
+    _check("smla_delta", lib().smla_delta(_ptr(o), _ptr(dO), _ptr(dlse), T, H, _ptr(delta),
+                                          _stream(o.device)))
     return delta
 
 

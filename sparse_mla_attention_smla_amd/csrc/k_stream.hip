@@ -3,6 +3,11 @@
 //
 // Page: aiter PR 4766 "Sparse MLA training backward", Structure table
 // ("delta = rowsum(O*dO)" streams bf16 and accumulates fp32; "d_sink").
+//
+// An upstream gradient of lse enters every later phase only through delta:
+// d lse / d S_k = P_k and d lse / d sink = P_sink, so dS = P (dP - delta + dlse)
+// and d_sink = -sum_t P_sink (delta - dlse).  The delta kernel therefore
+// stores delta - dlse when dlse is given, and nothing downstream changes.
 #include "smla_device.hpp"
 #include "smla_launch.hpp"
 
@@ -14,6 +19,7 @@ namespace smla {
 // are combined by a fixed xor-butterfly.
 __global__ __launch_bounds__(256) void smla_k1_delta(const uint16_t* __restrict__ O,
                                                      const uint16_t* __restrict__ dO,
+                                                     const float* __restrict__ dlse,
                                                      float* __restrict__ delta, int64_t rows) {
     const int lane = threadIdx.x & 63;
     const int sub = lane >> 4;
@@ -45,16 +51,16 @@ __global__ __launch_bounds__(256) void smla_k1_delta(const uint16_t* __restrict_
         acc += wave_xor(acc, 4);
         acc += wave_xor(acc, 2);
         acc += wave_xor(acc, 1);
-        if (l16 == 0 && r < rows) delta[r] = acc;
+        if (l16 == 0 && r < rows) delta[r] = dlse != nullptr ? acc - dlse[r] : acc;
     }
 }
 
-hipError_t launch_delta(const uint16_t* o, const uint16_t* dO, int64_t rows, float* delta,
-                        hipStream_t s) {
+hipError_t launch_delta(const uint16_t* o, const uint16_t* dO, const float* dlse, int64_t rows,
+                        float* delta, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     int64_t want = (rows + 15) / 16;              // 16 rows per 256-thread block step
     int blocks = (int)(want < 256 * 16 ? want : 256 * 16);
-    smla_k1_delta<<<blocks, 256, 0, s>>>(o, dO, delta, rows);
+    smla_k1_delta<<<blocks, 256, 0, s>>>(o, dO, dlse, delta, rows);
     return hipGetLastError();
 }
 

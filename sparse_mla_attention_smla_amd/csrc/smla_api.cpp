@@ -212,8 +212,8 @@ int smla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const fl
 }
 
 int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
-             const float* lse, const int32_t* idx, const float* sink, int T, int H, int num_kv,
-             int topk, float scale, uint16_t* dq, uint16_t* dkv, float* d_sink,
+             const float* lse, const int32_t* idx, const float* sink, const float* dlse, int T,
+             int H, int num_kv, int topk, float scale, uint16_t* dq, uint16_t* dkv, float* d_sink,
              int32_t* n_invalid, void* workspace, size_t workspace_bytes, void* stream) {
     smla_status st = check_shape(T, H, num_kv, topk);
     if (st != SMLA_OK) return st;
@@ -223,8 +223,8 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
     if ((sink == nullptr) != (d_sink == nullptr)) return SMLA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(dO, 16) || !aligned(o, 16) ||
         !aligned(dq, 16) || !aligned(dkv, 16) || !aligned(lse, 4) || !aligned(idx, 4) ||
-        !aligned(sink, 4) || !aligned(d_sink, 4) || !aligned(n_invalid, 4) ||
-        !aligned(workspace, 16))
+        !aligned(sink, 4) || !aligned(dlse, 4) || !aligned(d_sink, 4) ||
+        !aligned(n_invalid, 4) || !aligned(workspace, 16))
         return SMLA_ERR_ALIGN;
     const BwdLayout L = bwd_layout(T, H, num_kv, topk);
     if (workspace == nullptr || workspace_bytes < L.total) return SMLA_ERR_WORKSPACE;
@@ -237,12 +237,13 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
                          {lse, (size_t)T * H * 4},
                          {idx, (size_t)T * topk * 4},
                          {sink, sink ? hb : 0},
+                         {dlse, dlse ? (size_t)T * H * 4 : 0},
                          {dq, qb},
                          {dkv, (size_t)num_kv * kD * 2},
                          {d_sink, d_sink ? hb : 0},
                          {n_invalid, n_invalid ? 4u : 0u},
                          {workspace, L.total}};
-    if (!outputs_disjoint(all, 12, 7)) return SMLA_ERR_INVALID_ARG;
+    if (!outputs_disjoint(all, 13, 8)) return SMLA_ERR_INVALID_ARG;
     if ((st = check_arch()) != SMLA_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -273,7 +274,7 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
     }
     if (launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, aux) != hipSuccess) return SMLA_ERR_HIP;
     if (launch_gather_plan(row_ptr, M, num_kv, gs, aux) != hipSuccess) return SMLA_ERR_HIP;
-    if (launch_delta(o, dO, (int64_t)T * H, delta, s) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_delta(o, dO, dlse, (int64_t)T * H, delta, s) != hipSuccess) return SMLA_ERR_HIP;
     if (sink != nullptr) {
         if (side != nullptr && (hipEventRecord(side->after_delta, s) != hipSuccess ||
                                 hipStreamWaitEvent(aux, side->after_delta, 0) != hipSuccess))
@@ -292,16 +293,20 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
     return SMLA_OK;
 }
 
-int smla_delta(const uint16_t* o, const uint16_t* dO, int T, int H, float* delta, void* stream) {
+int smla_delta(const uint16_t* o, const uint16_t* dO, const float* dlse, int T, int H,
+               float* delta, void* stream) {
     smla_status st = check_shape(T, H, T > 0 ? T : 1, 1);
     if (st != SMLA_OK) return st;
     if (T > 0 && (!o || !dO || !delta)) return SMLA_ERR_INVALID_ARG;
-    if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(delta, 4)) return SMLA_ERR_ALIGN;
+    if (!aligned(o, 16) || !aligned(dO, 16) || !aligned(dlse, 4) || !aligned(delta, 4))
+        return SMLA_ERR_ALIGN;
     const size_t qb = (size_t)T * H * kD * 2;
-    const Range all[] = {{o, qb}, {dO, qb}, {delta, (size_t)T * H * 4}};
-    if (!outputs_disjoint(all, 3, 2)) return SMLA_ERR_INVALID_ARG;
+    const size_t rb = (size_t)T * H * 4;
+    const Range all[] = {{o, qb}, {dO, qb}, {dlse, dlse ? rb : 0}, {delta, rb}};
+    if (!outputs_disjoint(all, 4, 3)) return SMLA_ERR_INVALID_ARG;
     if ((st = check_arch()) != SMLA_OK) return st;
-    return hip_status(launch_delta(o, dO, (int64_t)T * H, delta, static_cast<hipStream_t>(stream)));
+    return hip_status(
+        launch_delta(o, dO, dlse, (int64_t)T * H, delta, static_cast<hipStream_t>(stream)));
 }
 
 int smla_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const float* lse,

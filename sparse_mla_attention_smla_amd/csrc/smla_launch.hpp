@@ -12,8 +12,9 @@ namespace smla {
 hipError_t compute_units(int* n);
 
 // ---- streaming ------------------------------------------------------------
-hipError_t launch_delta(const uint16_t* o, const uint16_t* dO, int64_t rows, float* delta,
-                        hipStream_t s);
+// delta[r] = sum_d o[r,d] * dO[r,d], minus dlse[r] when dlse is not null
+hipError_t launch_delta(const uint16_t* o, const uint16_t* dO, const float* dlse, int64_t rows,
+                        float* delta, hipStream_t s);
 constexpr int kDsinkTokensPerBlock = 32;
 inline int dsink_blocks(int T) { return (T + kDsinkTokensPerBlock - 1) / kDsinkTokensPerBlock; }
 hipError_t launch_dsink(const float* lse, const float* delta, const float* sink, int T, int H,

@@ -27,6 +27,9 @@ Recipe (seed s = 1000 + workload.index):
   2**22 values; chunk c of tensor k (q=1, kv=2, dO=3) comes from
   ``np.random.default_rng([s, k, c])``, so chunks can be drawn in parallel
   threads and the result does not depend on the thread count.
+* dlse (an optional upstream gradient of lse, [T,H] float32) -- standard normal
+  from ``np.random.default_rng([s, 4])``; its spread is that of delta for these
+  inputs, so both terms of the shifted delta matter.
 """
 from __future__ import annotations
 
@@ -162,6 +165,12 @@ def make(name_or_workload, sink: bool = True) -> dict:
     kv = normal_bf16((w.num_kv, D), seed, 2)
     dO = normal_bf16((w.T, w.H, D), seed, 3)
     return {"workload": w, "q": q, "kv": kv, "dO": dO, "idx": idx, "sink": s if sink else None}
+
+
+def make_dlse(name_or_workload) -> np.ndarray:
+    """Seeded upstream gradient of lse for one workload: float32 [T, H]."""
+    w = WORKLOADS[name_or_workload] if isinstance(name_or_workload, str) else name_or_workload
+    return np.random.default_rng([1000 + w.index, 4]).standard_normal((w.T, w.H), dtype=np.float32)
 
 
 def shuffle_slots(idx: np.ndarray, seed: int) -> np.ndarray:

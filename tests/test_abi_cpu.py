@@ -68,9 +68,10 @@ A = 0x10000000  # fake, 256-B aligned device addresses (never dereferenced)
 
 def _bwd(lib, T=64, H=16, N=64, K=16, scale=0.05, sink=True, d_sink=True, ws=1 << 34, **ptr):
     p = dict(q=A, kv=2 * A, dO=3 * A, o=4 * A, lse=5 * A, idx=6 * A, sink=7 * A if sink else None,
-             dq=8 * A, dkv=9 * A, d_sink=10 * A if d_sink else None, n_inv=None, work=11 * A)
+             dlse=None, dq=8 * A, dkv=9 * A, d_sink=10 * A if d_sink else None, n_inv=None, work=11 * A)
     p.update(ptr)
-    return lib.smla_bwd(p["q"], p["kv"], p["dO"], p["o"], p["lse"], p["idx"], p["sink"], T, H, N, K,
+    return lib.smla_bwd(p["q"], p["kv"], p["dO"], p["o"], p["lse"], p["idx"], p["sink"], p["dlse"],
+                        T, H, N, K,
                         scale, p["dq"], p["dkv"], p["d_sink"], p["n_inv"], p["work"], ws, None)
 
 
@@ -91,14 +92,19 @@ def test_bwd_argument_errors(lib):
     assert _bwd(lib, ws=1024) == WORKSPACE
     assert _bwd(lib, dq=A) == INVALID                     # dq aliases q
     assert _bwd(lib, work=9 * A + 4096) == INVALID        # workspace inside dkv
+    assert _bwd(lib, dlse=12 * A + 2) == ALIGN
+    assert _bwd(lib, n_inv=8 * A + 64) == INVALID         # n_invalid inside dq
+    assert _bwd(lib, dlse=12 * A) in (HIP, ARCH)          # dlse is optional
     # a valid call gets past validation and then needs a gfx950 device
     assert _bwd(lib) in (HIP, ARCH)
 
 
 def test_stage_argument_errors(lib):
-    assert lib.smla_delta(A, 2 * A, 4, 16, A, None) == INVALID          # delta aliases o
-    assert lib.smla_delta(A, 2 * A, 4, 20, 3 * A, None) == SHAPE
-    assert lib.smla_delta(A + 8, 2 * A, 4, 16, 3 * A, None) == ALIGN
+    assert lib.smla_delta(A, 2 * A, None, 4, 16, A, None) == INVALID          # delta aliases o
+    assert lib.smla_delta(A, 2 * A, 3 * A, 4, 16, 3 * A, None) == INVALID     # delta aliases dlse
+    assert lib.smla_delta(A, 2 * A, None, 4, 20, 3 * A, None) == SHAPE
+    assert lib.smla_delta(A + 8, 2 * A, None, 4, 16, 3 * A, None) == ALIGN
+    assert lib.smla_delta(A, 2 * A, 4 * A + 2, 4, 16, 3 * A, None) == ALIGN
     assert lib.smla_build_csr(A, 4, 16, 3, 2 * A, 3 * A, None, 4 * A, 1 << 30, None) == SHAPE
     assert lib.smla_build_csr(A, 4, 16, 8, 2 * A, 3 * A, None, 4 * A, 8, None) == WORKSPACE
     assert lib.smla_gather(A, 2 * A, 3 * A, 4, 16, 8, 4 * A, None, 0, None) == WORKSPACE

@@ -76,6 +76,25 @@ def test_stage_delta(small_case):
     delta = B.smla_delta(d["O"], d["dO"])
     torch.cuda.synchronize()
     assert rel_l2(delta.cpu().numpy(), ref["delta"]) < 1e-5
+    dlse = inputs.make_dlse(name.replace("_nosink", ""))
+    shifted = B.smla_delta(d["O"], d["dO"], dlse=dev(dlse))
+    torch.cuda.synchronize()
+    assert rel_l2(shifted.cpu().numpy(), ref["delta"] - dlse) < 1e-5
+
+
+def test_end_to_end_with_dlse(small_case):
+    """An upstream gradient of lse: dS gains P*dlse, d_sink gains P_sink*dlse."""
+    name, x, ref, d = small_case
+    dlse = inputs.make_dlse(name.replace("_nosink", ""))
+    want = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE,
+                        dlse=dlse)
+    dq, dkv, ds = _run_bwd(d, dlse=dev(dlse))
+    assert_close(f"{name} dq (dlse)", host_bf16(dq), want["dq"])
+    assert_close(f"{name} dkv (dlse)", host_bf16(dkv), want["dkv"])
+    if x["sink"] is not None:
+        assert_close(f"{name} d_sink (dlse)", ds.cpu().numpy(), want["d_sink"])
+    # the term is not negligible: it moves dq by several times the tolerance
+    assert rel_l2(want["dq"], ref["dq"]) > 4 * 5e-3
 
 
 def test_stage_dq_and_dsp(small_case):
@@ -260,20 +279,25 @@ def _oracle_inputs(x):
     return x
 
 
-@pytest.mark.parametrize("T,H,N,K,sink", [
-    (37, 48, 53, 40, True),     # 3-wave head groups, ragged 32-slot tail, pool rows
-    (20, 32, 20, 1, True),      # topk = 1
-    (33, 80, 40, 70, False),    # 1-wave head groups, no sink
-    (17, 112, 30, 33, True),
-    (9, 128, 300, 96, True),    # most kv rows unused
+@pytest.mark.parametrize("T,H,N,K,sink,with_dlse", [
+    (37, 48, 53, 40, True, False),    # 3-wave head groups, ragged 32-slot tail, pool rows
+    (20, 32, 20, 1, True, False),     # topk = 1
+    (33, 80, 40, 70, False, False),   # 1-wave head groups, no sink
+    (17, 112, 30, 33, True, False),
+    (9, 128, 300, 96, True, False),   # most kv rows unused
+    (37, 48, 53, 40, True, True),     # with dlse: the all-masked row gets P_sink = 1
+    (33, 80, 40, 70, False, True),    # with dlse, no sink: the all-masked row stays zero
 ])
-def test_ragged_shapes(T, H, N, K, sink):
+def test_ragged_shapes(T, H, N, K, sink, with_dlse):
     x = _custom(T, H, N, K, seed=T * 1000 + H, sink=sink, pool_frac=0.5)
     x["idx"][3] = -1                                    # one all-masked row
     x = _oracle_inputs(x)
-    _say(f"[ragged] T={T} H={H} N={N} K={K} sink={sink}")
-    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE)
-    dq, dkv, ds = _run_bwd(_to_dev(x))
+    _say(f"[ragged] T={T} H={H} N={N} K={K} sink={sink} dlse={with_dlse}")
+    dlse = (np.random.default_rng(T + H).standard_normal((T, H)).astype(np.float32)
+            if with_dlse else None)
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE,
+                       dlse=dlse)
+    dq, dkv, ds = _run_bwd(_to_dev(x), dlse=None if dlse is None else dev(dlse))
     assert_close("dq", host_bf16(dq), ref["dq"])
     assert_close("dkv", host_bf16(dkv), ref["dkv"])
     assert np.all(host_bf16(dq)[3] == 0.0)
@@ -343,14 +367,16 @@ def test_error_codes_from_device_side_entry():
 # full-size workloads (the benchmark's launch configuration), sampled outputs
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["headline", "skewed", "long"])
-def test_full_size_sampled(name):
-    _say(f"[full] {name}: generating inputs and the oracle forward")
+@pytest.mark.parametrize("name,with_dlse", [("headline", False), ("skewed", False), ("long", False),
+                                            ("headline", True)])
+def test_full_size_sampled(name, with_dlse):
+    _say(f"[full] {name}: generating inputs and the oracle forward (dlse={with_dlse})")
     x = workload(name)
     w = x["workload"]
     d = _to_dev(x)
+    dlse = inputs.make_dlse(name) if with_dlse else None
     _say(f"[full] {name}: running smla_bwd")
-    dq, dkv, ds = _run_bwd(d)
+    dq, dkv, ds = _run_bwd(d, dlse=None if dlse is None else dev(dlse))
     # CSR: bit-exact at full size
     row_ptr, slots = B.smla_build_csr(d["idx"], w.num_kv)
     rp, sl = orc.csr(x["idx"], w.num_kv)
@@ -359,7 +385,8 @@ def test_full_size_sampled(name):
     # dq on sampled tokens
     rng = np.random.default_rng(w.index)
     toks = sorted(set([0, 1, 127, 128, 1535, w.T // 2, w.T - 1] + list(rng.integers(0, w.T, 9))))
-    r = orc.backward_tokens(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, toks)
+    r = orc.backward_tokens(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, toks,
+                            dlse=dlse)
     assert_close(f"{name} dq sampled", host_bf16(dq[toks]), r["dq"])
     # dkv on sampled rows: token rows, the busiest pool row, a lightly used pool row
     counts = np.diff(rp)
@@ -368,12 +395,14 @@ def test_full_size_sampled(name):
     light = int(pool[np.argmin(np.where(counts[w.T:] > 0, counts[w.T:], 1 << 30))])
     rows = sorted(set([0, 5, w.T // 3, w.T - 1, busiest, light] + list(rng.integers(0, w.num_kv, 4))))
     _say(f"[full] {name}: oracle dkv on rows {rows} (contributors {counts[rows].tolist()})")
-    want = orc.dkv_rows(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, rows)
+    want = orc.dkv_rows(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, rows,
+                        dlse=dlse)
     assert_close(f"{name} dkv sampled", host_bf16(dkv[rows]), want)
     empty = np.nonzero(counts == 0)[0]
     if empty.size:
         assert np.all(host_bf16(dkv[torch.as_tensor(empty[:64], device='cuda')]) == 0.0)
     # d_sink: every token contributes
-    assert_close(f"{name} d_sink", ds.cpu().numpy(), orc.d_sink(x["dO"], x["O"], x["lse"], x["sink"]))
+    assert_close(f"{name} d_sink", ds.cpu().numpy(),
+                 orc.d_sink(x["dO"], x["O"], x["lse"], x["sink"], dlse=dlse))
     del d
     torch.cuda.empty_cache()
