@@ -245,6 +245,26 @@ def main():
                 "unit": unit, "frac": round(achieved / peak, 4), "traffic": stored_traffic(dom),
                 "algorithmic_per_launch": work, "ms_per_launch": round(tms, 4)}
 
+    # the forward that produces O and lse (not part of the step; reported beside it)
+    o2 = torch.empty_like(q)
+    lse2 = torch.empty((T, H), dtype=torch.float32, device="cuda")
+
+    def fwd():
+        B.smla_fwd(q, kv, idx, sink, scale, out=(o2, lse2))
+    fwd()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.stage_steps):
+        fwd()
+    b.record()
+    torch.cuda.synchronize()
+    fwd_ms = a.elapsed_time(b) / args.stage_steps
+    fwd_tf = 4.0 * T * H * K * D / (fwd_ms * 1e-3) / 1e12
+    forward = {"ms": round(fwd_ms, 4), "bound": "mfma", "achieved_tflops": round(fwd_tf, 1),
+               "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+               "note": "smla_fwd (O and lse) on the same inputs; nominal 4*T*H*topk*512 flops"}
+
     cpu = None
     if args.cpu_baseline == "on":
         print(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr,
@@ -273,6 +293,7 @@ def main():
                    "global_batch": T, "seq_len": T, "parallelism": "none (1 GPU)",
                    "valid_slots": nnz},
         "stages": stage_rows,
+        "forward": forward,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "context": {"pages_own_backward_mi355x": {"ms": 3.238, "tflops": 424},

@@ -109,8 +109,9 @@ def _default_scale(scale):
 # forward / backward
 # ---------------------------------------------------------------------------
 
-def smla_fwd(q, kv, idx, sink=None, scale=None):
-    """Sparse MLA forward: (o bf16 [T,H,512], lse fp32 [T,H]).  lse includes the sink."""
+def smla_fwd(q, kv, idx, sink=None, scale=None, out=None):
+    """Sparse MLA forward: (o bf16 [T,H,512], lse fp32 [T,H]).  lse includes the sink.
+    out, if given, is a tuple (o, lse) of preallocated outputs."""
     T, H, _ = q.shape
     N, K = kv.shape[0], idx.shape[1]
     _need(q, "q", torch.bfloat16, (T, H, D))
@@ -118,8 +119,13 @@ def smla_fwd(q, kv, idx, sink=None, scale=None):
     _need(idx, "idx", torch.int32, (T, K))
     if sink is not None:
         _need(sink, "sink", torch.float32, (H,))
-    o = torch.empty_like(q)
-    lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _need(o, "o", torch.bfloat16, (T, H, D))
+        _need(lse, "lse", torch.float32, (T, H))
     _check("smla_fwd", lib().smla_fwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(sink), T, H, N, K,
                                       _default_scale(scale), _ptr(o), _ptr(lse), _stream(q.device)))
     return o, lse

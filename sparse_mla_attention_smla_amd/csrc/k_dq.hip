@@ -220,8 +220,15 @@ struct ItemSeq {
 struct DqShared {
     char* tiles;        // kNBuf ring slots of kTileBytes
     SlotList* Lb;       // [2] slot lists, segment s uses Lb[s & 1]
-    u32x4 (*dsfrag)[4][64];  // [2][4][64] dS fragments: [position parity][producer][lane]
+    u32x4 (*dsfrag)[4][64];  // [2][4][64] dS (forward: P) fragments: [position parity][producer][lane]
     char* touch;             // 1 KiB landing area of the cache-warming copies (never read)
+    // forward only, [position parity][producer]: whether the producer moved the
+    // reference max of any of its heads at that tile, the factors by which the
+    // output accumulators of its 16 heads are rescaled, and at an item's last
+    // tile the output scale 1/sum of each head
+    int (*resc)[4];
+    float (*alpha)[4][16];
+    float (*oscale)[4][16];
 };
 
 constexpr int kMinStream = 5;  // segments this long hand over to the next without a drain
@@ -254,12 +261,19 @@ __device__ __forceinline__ void settle_scalars(float a, float b) {
     asm volatile("" : : "v"(a), "v"(b));
 }
 
-template <bool PROD>
+// FWD selects the forward pass on the same stream: the producers compute only
+// S^T and keep an online softmax per head (lse, written at the item's last
+// tile); the consumers accumulate O^T = kv^T . P^T and scale it by 1/sum in
+// their epilogue.  Then dO, delta and dsp are unused, lse is written (not
+// read), dq receives O, and the forward needs one segment per item (topk <= 512).
+template <bool PROD, bool FWD>
 __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                            const uint16_t* __restrict__ dO, const float* __restrict__ lse,
                                            const float* __restrict__ delta, const int32_t* __restrict__ idx,
                                            int T, int H, int N, int K, float scale, uint16_t* __restrict__ dq,
-                                           uint16_t* __restrict__ dsp, const DqShared sh, int w, int lane) {
+                                           uint16_t* __restrict__ dsp, const DqShared sh, int w, int lane,
+                                           const float* __restrict__ sink = nullptr,
+                                           float* __restrict__ lse_out = nullptr) {
     constexpr int R = kBK / 4;   // copies per consumer wave per tile
     constexpr int kEpiStores = 32;  // global stores of one consumer epilogue (4 heads x 8 d-blocks)
     constexpr int kWarmTiles = 8;   // tiles over which the next item's q/dO are warmed (32 chunks)
@@ -279,9 +293,15 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     u32x4 qf[16], dof[16];
     float bias = 0.f, dl = 0.f;     // of the item being produced
     float nbias = 0.f, ndl = 0.f;   // of the next item, loaded with its q/dO
+    // forward: bias/nbias hold the head's sink logit in log2 units (-inf: none);
+    // online softmax state of this lane's head, in log2 units
+    constexpr float kLazy = 8.f;    // the reference max moves only when exceeded by this
+    float m_use = -INFINITY;        // reference max the exponents are taken against
+    float l_run = 0.f;              // this lane's share of the sum, relative to m_use
     int p_n = 0;                    // valid slots of the segment being produced
     int p_ctg = 0;                  // compacted tiles of the item before that segment
     int p_h = 0;                    // head of this lane
+    size_t p_item_row = 0;          // forward: row of lse_out of the wave's first head
     uint16_t* p_blk = dsp;          // dsp block of the item's compacted tile 0
     const float c = scale * kLog2e;
     auto item_rows = [&](int item, int& h, size_t& lrow) {
@@ -290,6 +310,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         lrow = (size_t)t * H + h;
     };
     auto bias_of = [](float l) { return (l == -INFINITY) ? INFINITY : l * kLog2e; };
+    auto sink_of = [&](int h) { return sink != nullptr ? sink[h] * kLog2e : -INFINITY; };
     // first element of this lane's load row (lane 4*c16 + g: head c16, chunk g)
     auto frag_src = [&](int item) {
         const int t = item / nhg, hg = item - t * nhg;
@@ -303,15 +324,37 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
 #pragma unroll
         for (int ds = 0; ds < 16; ++ds) {
             qf[ds] = *reinterpret_cast<const u32x4*>(q + src + 32 * ds);
-            dof[ds] = *reinterpret_cast<const u32x4*>(dO + src + 32 * ds);
+            if constexpr (!FWD) dof[ds] = *reinterpret_cast<const u32x4*>(dO + src + 32 * ds);
         }
-        nbias = bias_of(lse[lrow]);
-        ndl = delta[lrow];
+        if constexpr (FWD) {
+            nbias = sink_of(h);
+        } else {
+            nbias = bias_of(lse[lrow]);
+            ndl = delta[lrow];
+        }
     };
     auto finish_load = [&]() {
         frag_to_mfma_lanes(qf, lane);
-        frag_to_mfma_lanes(dof, lane);
+        if constexpr (!FWD) frag_to_mfma_lanes(dof, lane);
         settle_scalars(nbias, ndl);
+    };
+    // forward: lse of the item whose last tile was just produced (or that has no
+    // valid slot), with the sink folded in; returns the output scale a/z of the head
+    auto finish_softmax = [&]() -> float {
+        float l_tot = l_run + wave_xor(l_run, 16);
+        l_tot += wave_xor(l_tot, 32);
+        const float m_fin = fmaxf(m_use, bias);
+        float osc = 0.f, lse_v = -INFINITY;
+        if (m_fin != -INFINITY) {
+            const float a = __builtin_amdgcn_exp2f(m_use - m_fin);
+            const float z = l_tot * a + __builtin_amdgcn_exp2f(bias - m_fin);
+            osc = a / z;
+            lse_v = (m_fin + log2f(z)) * kLn2;
+        }
+        if (g == 0) lse_out[p_item_row + c16] = lse_v;
+        m_use = -INFINITY;
+        l_run = 0.f;
+        return osc;
     };
     // point the producer at segment s (its slot list must be visible)
     auto enter_segment = [&](int s, bool new_item) {
@@ -320,7 +363,12 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         item_rows(item, p_h, lrow);
         if (new_item) { bias = nbias; dl = ndl; p_ctg = 0; }
         p_n = Lb[s & 1].n;
-        p_blk = dsp + (size_t)(item / nhg) * ntk * (2 * H) * kBK;
+        if constexpr (FWD) {
+            p_item_row = lrow - c16;
+            if (p_n == 0) (void)finish_softmax();   // no valid slot: only lse is written
+        } else {
+            p_blk = dsp + (size_t)(item / nhg) * ntk * (2 * H) * kBK;
+        }
     };
     // S^T, dP^T of tile jt of the producer's segment (ring position pos) -> P,
     // scale*dS (stored) -> dS fragment into LDS.  With RELOAD, each d-chunk of
@@ -352,39 +400,86 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
                 sacc[st] = mfma16(ab[ds][st], qf[ds], sacc[st]);
-                pacc[st] = mfma16(ab[ds][st], dof[ds], pacc[st]);
+                if constexpr (!FWD) pacc[st] = mfma16(ab[ds][st], dof[ds], pacc[st]);
             }
             if (ds + PF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, FWD ? 2 : 4, 0);
             if constexpr (decltype(reload)::value) {
                 qf[ds] = *reinterpret_cast<const u32x4*>(nq + 32 * ds);
-                dof[ds] = *reinterpret_cast<const u32x4*>(nd + 32 * ds);
+                if constexpr (!FWD) dof[ds] = *reinterpret_cast<const u32x4*>(nd + 32 * ds);
             }
         }
-        float dss[2][4], ps[2][4];
+        if constexpr (FWD) {
+            // Online softmax with a lazily moved reference max: exponents are
+            // taken against m_use, which moves only when a logit of the head
+            // exceeds it by more than kLazy, so P <= 2^kLazy and the consumers
+            // rescale their accumulators only at such moves (rare after the first
+            // tile).  The lane's 8 logits belong to head c16; the other three
+            // lanes of that head are lane ^ 16 and lane ^ 32.
+            float x[2][4];
+            float tmax = -INFINITY;
 #pragma unroll
-        for (int st = 0; st < 2; ++st)
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool v = jt * kBK + 16 * st + 4 * g + i < p_n;
-                const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[st][i], c, -bias)) : 0.f;
-                ps[st][i] = p;
-                dss[st][i] = p * (pacc[st][i] - dl) * scale;
+                for (int i = 0; i < 4; ++i) {
+                    const bool v = jt * kBK + 16 * st + 4 * g + i < p_n;
+                    x[st][i] = v ? sacc[st][i] * c : -INFINITY;
+                    tmax = fmaxf(tmax, x[st][i]);
+                }
+            tmax = fmaxf(tmax, wave_xor(tmax, 16));
+            tmax = fmaxf(tmax, wave_xor(tmax, 32));
+            // every tile holds a valid slot, so tmax is finite and the first tile moves
+            const bool move = tmax > m_use + kLazy;
+            const float m_new = move ? tmax : m_use;
+            const float alpha = __builtin_amdgcn_exp2f(m_use - m_new);   // 1, or 0 from -inf
+            const bool rescale = move && m_use != -INFINITY;            // accumulators hold data
+            l_run *= alpha;
+            m_use = m_new;
+            float ps[2][4];
+#pragma unroll
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    ps[st][i] = __builtin_amdgcn_exp2f(x[st][i] - m_use);
+                    l_run += ps[st][i];
+                }
+            const int par = pos & 1;
+            const bool any = __ballot(rescale) != 0ull;
+            if (any && g == 0) sh.alpha[par][w][c16] = alpha;
+            if (lane == 0) sh.resc[par][w] = any ? 1 : 0;
+            sh.dsfrag[par][w][lane] =
+                u32x4{pack_bf16(ps[0][0], ps[0][1]), pack_bf16(ps[0][2], ps[0][3]),
+                      pack_bf16(ps[1][0], ps[1][1]), pack_bf16(ps[1][2], ps[1][3])};
+            if (jt == (p_n + kBK - 1) / kBK - 1) {
+                const float osc = finish_softmax();
+                if (g == 0) sh.oscale[par][w][c16] = osc;
             }
-        // dsp rows of this wave's 16 heads, quad-contiguous: lane 4*c + g stores
-        // head (p_h - c16 + c), columns 16st + 4g .. +3
-        uint16_t* blk = p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK +
-                        (size_t)(p_h - c16 + (lane >> 2)) * kBK + 4 * (lane & 3);
+        } else {
+            float dss[2][4], ps[2][4];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-            *reinterpret_cast<u32x2*>(blk + 16 * st) = to_quad_rows(
-                u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])}, lane);
-            *reinterpret_cast<u32x2*>(blk + (size_t)H * kBK + 16 * st) = to_quad_rows(
-                u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])}, lane);
+            for (int st = 0; st < 2; ++st)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool v = jt * kBK + 16 * st + 4 * g + i < p_n;
+                    const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[st][i], c, -bias)) : 0.f;
+                    ps[st][i] = p;
+                    dss[st][i] = p * (pacc[st][i] - dl) * scale;
+                }
+            // dsp rows of this wave's 16 heads, quad-contiguous: lane 4*c + g stores
+            // head (p_h - c16 + c), columns 16st + 4g .. +3
+            uint16_t* blk = p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK +
+                            (size_t)(p_h - c16 + (lane >> 2)) * kBK + 4 * (lane & 3);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                *reinterpret_cast<u32x2*>(blk + 16 * st) = to_quad_rows(
+                    u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])}, lane);
+                *reinterpret_cast<u32x2*>(blk + (size_t)H * kBK + 16 * st) = to_quad_rows(
+                    u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])}, lane);
+            }
+            sh.dsfrag[pos & 1][w][lane] =
+                u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
+                      pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
         }
-        sh.dsfrag[pos & 1][w][lane] =
-            u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
-                  pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
     };
     using NoReload = std::integral_constant<bool, false>;
     using Reload = std::integral_constant<bool, true>;
@@ -410,7 +505,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     // one when there is nothing to warm), which keeps the vmcnt bounds exact.
     const uint32_t touch_lds = lds_addr(sh.touch);
     auto touch = [&](int item_next, int k) {
-        const bool real = item_next >= 0 && k >= 0 && k < 32;
+        const bool real = item_next >= 0 && k >= 0 && k < (FWD ? 16 : 32);   // forward: q only
         const int it = real ? item_next : 0;
         const int t = it / nhg, hg = it - t * nhg;
         const uint16_t* rows = (k < 16 ? q : dO) + ((size_t)t * H + hg * 64) * kD;
@@ -418,6 +513,18 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     };
     auto consume = [&](int pos) {
         const int cb = cols_base(c16, g);
+        if constexpr (FWD) {
+            // lane c16 + 16g of acc[.][m] belongs to head 16m + c16: apply the
+            // producers' rescale factors before this tile's P is added
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                if (__builtin_amdgcn_readfirstlane(sh.resc[pos & 1][m])) {
+                    const float a = sh.alpha[pos & 1][m][c16];
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt) acc[dt][m] *= a;
+                }
+            }
+        }
         u32x4 b[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) b[m] = sh.dsfrag[pos & 1][m][lane];
@@ -438,16 +545,22 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     };
     // lane c16 + 16g holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16;
     // stored quad-contiguous (lane 4*c + g writes head 16m + c)
-    auto epilogue = [&](int item) {
+    // Forward: the output is scaled by the producers' 1/sum of the head, published
+    // with the item's last tile at position pos_last (-1: the item has no tile).
+    auto epilogue = [&](int item, int pos_last) {
         const int t = item / nhg, hg = item - t * nhg;
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int h = hg * 64 + 16 * m + (lane >> 2);
             uint16_t* out = dq + ((size_t)t * H + h) * kD + 128 * dq4 + 4 * (lane & 3);
+            float sc = 0.f;
+            if constexpr (FWD) sc = pos_last >= 0 ? sh.oscale[pos_last & 1][m][c16] : 0.f;
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
-                *reinterpret_cast<u32x2*>(out + 16 * dt) = to_quad_rows(
-                    u32x2{pack_bf16(acc[dt][m][0], acc[dt][m][1]), pack_bf16(acc[dt][m][2], acc[dt][m][3])}, lane);
+                f32x4 v = acc[dt][m];
+                if constexpr (FWD) v *= sc;
+                *reinterpret_cast<u32x2*>(out + 16 * dt) =
+                    to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane);
                 acc[dt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -523,8 +636,12 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                         item_rows(nitem, h, lrow);
                         const size_t src = frag_src(nitem);
                         produce(pos + 1, j + 1, Reload{}, q + src, dO + src);
-                        nbias = bias_of(lse[lrow]);
-                        ndl = delta[lrow];
+                        if constexpr (FWD) {
+                            nbias = sink_of(h);
+                        } else {
+                            nbias = bias_of(lse[lrow]);
+                            ndl = delta[lrow];
+                        }
                         finish_load();
                     } else {
                         produce(pos + 1, j + 1, NoReload{}, nullptr, nullptr);
@@ -549,7 +666,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 if (post_epi > 0) --post_epi;
                 ++since;
                 if (j + 1 == ntile && last_of_item) {
-                    epilogue(item);
+                    epilogue(item, pos);
                     post_epi = 2;
                 }
                 if (w == 4 && has_next && ntile >= 2 && j == 0) load_slot_chunk(idx_next, K, k0_next, nxt, lane);
@@ -566,7 +683,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 }
             } else {
                 if (w == 4 && has_next && ntile < 2) compact_slots(idx_next, K, N, k0_next, &Lb[(s + 1) & 1], lane);
-                if (ntile == 0 && last_of_item) epilogue(item);
+                if (ntile == 0 && last_of_item) epilogue(item, -1);
                 wait_vmcnt<0>();
                 post_epi = 0;
             }
@@ -589,11 +706,48 @@ void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     __shared__ SlotList Lb[2];
     __shared__ u32x4 dsfrag[2][4][64];
     __shared__ __attribute__((aligned(16))) char touch[1024];
-    const DqShared sh{tiles, Lb, dsfrag, touch};
+    const DqShared sh{tiles, Lb, dsfrag, touch, nullptr, nullptr, nullptr};
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    if (w < 4) dq_pc_role<true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
-    else dq_pc_role<false>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
+    if (w < 4) dq_pc_role<true, false>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
+    else dq_pc_role<false, false>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
+}
+
+// Forward on the same persistent stream (64-head groups, topk <= 512): o and
+// lse for every (token, head).
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k7_fwd_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                    const int32_t* __restrict__ idx, const float* __restrict__ sink, int T, int H,
+                    int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    static_assert(kNBuf == 4, "the stream assumes a 4-deep ring");
+    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    __shared__ int resc[2][4];
+    __shared__ float alpha[2][4][16];
+    __shared__ float oscale[2][4][16];
+    const DqShared sh{tiles, Lb, dsfrag, touch, resc, alpha, oscale};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh, w,
+                               lane, sink, lse);
+    else
+        dq_pc_role<false, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh, w,
+                                lane, sink, lse);
+}
+
+hipError_t launch_fwd_pc(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
+                         int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
+                         hipStream_t s) {
+    const int items = T * (H / 64);
+    int cus = 0;
+    const hipError_t e = compute_units(&cus);
+    if (e != hipSuccess) return e;
+    const unsigned blocks = (unsigned)(items < cus ? items : cus);
+    smla_k7_fwd_pc<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse);
+    return hipGetLastError();
 }
 
 // Heads per workgroup: 64, 32 or 16 (whichever divides H first).

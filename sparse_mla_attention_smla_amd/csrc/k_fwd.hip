@@ -138,11 +138,17 @@ void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
 }
 
 int dq_waves(int H);
+hipError_t launch_fwd_pc(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
+                         int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
+                         hipStream_t s);
 
 hipError_t launch_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
                       int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
                       hipStream_t s) {
     if (T == 0) return hipSuccess;
+    // 64-head groups with one index chunk per token: the persistent kernel
+    // (k_dq.hip) that shares the dQ pass's tile stream and wave roles
+    if (H % 64 == 0 && K <= kChunk) return launch_fwd_pc(q, kv, idx, sink, T, H, N, K, scale, o, lse, s);
     const int nw = dq_waves(H);
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
     switch (nw) {

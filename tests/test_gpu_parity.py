@@ -255,6 +255,72 @@ def test_forward_matches_oracle(name, sink):
     assert np.max(np.abs(got - lse64)) < 1e-4
 
 
+@pytest.mark.parametrize("T,H,N,K,sink", [
+    (40, 64, 70, 512, True),    # one full 512-slot chunk, ragged last tile, empty rows
+    (23, 128, 60, 33, False),   # two 64-head groups, 2 tiles per token, no sink
+    (50, 64, 50, 1, True),      # topk = 1: every token has at most one tile
+    (9, 64, 300, 96, True),     # most kv rows unused
+])
+def test_forward_ragged(T, H, N, K, sink):
+    x = _custom(T, H, N, K, seed=7 * T + H, sink=sink, pool_frac=0.5)
+    x["idx"][2] = -1                                    # an all-masked token
+    _say(f"[fwd ragged] T={T} H={H} N={N} K={K} sink={sink}")
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    s = dev(x["sink"]) if sink else None
+    o, lse = B.smla_fwd(dev_bf16(x["q"]), dev_bf16(x["kv"]), dev(x["idx"]), s, SCALE)
+    torch.cuda.synchronize()
+    got_o = host_bf16(o)
+    assert_close("O", got_o, O64)
+    got = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(lse64)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.max(np.abs(got[fin] - lse64[fin])) < 1e-4
+    assert np.all(got_o[2] == 0.0)
+    if sink:
+        # no valid slot: lse is the sink (to fp32 rounding of the log2-domain round trip)
+        np.testing.assert_allclose(got[2], x["sink"].astype(np.float64), rtol=1e-6, atol=1e-7)
+
+
+def test_forward_rising_logits_rescale_path():
+    """Logits that grow along the slot order by far more than the lazy-rescale
+    threshold for some heads (every tile moves the reference max), stay flat or
+    fall for others: both the rescaled and the untouched accumulators must
+    match the oracle."""
+    T, H, N, K = 6, 64, 520, 512
+    rng = np.random.default_rng(17)
+    u = rng.standard_normal(512)
+    a = np.linspace(-1.0, 1.5, H)                      # per-head slope of the logits
+    q = np.stack([a[:, None] * u[None, :]] * T)        # [T,H,512]
+    kv = (np.arange(N)[:, None] / 64.0) * u[None, :] + 0.05 * rng.standard_normal((N, 512))
+    idx = np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    idx[1, 300:] = -1
+    idx[3] = np.sort(rng.choice(N, K, replace=False)).astype(np.int32)
+    qb, kvb = orc.f64_to_bf16_rne(q), orc.f64_to_bf16_rne(kv)
+    sink = rng.standard_normal(H).astype(np.float32)
+    O64, lse64 = orc.forward(qb, kvb, idx, sink, SCALE)
+    o, lse = B.smla_fwd(dev_bf16(qb), dev_bf16(kvb), dev(idx), dev(sink), SCALE)
+    torch.cuda.synchronize()
+    assert_close("O (rising logits)", host_bf16(o), O64)
+    got = lse.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - lse64) / np.maximum(1.0, np.abs(lse64))) < 1e-5
+
+
+def test_forward_full_size_sampled():
+    x = workload("headline")
+    w = x["workload"]
+    _say("[fwd full] headline")
+    o, lse = B.smla_fwd(dev_bf16(x["q"]), dev_bf16(x["kv"]), dev(x["idx"]), dev(x["sink"]), SCALE)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(23)
+    toks = sorted(set([0, 1, 127, 128, w.T // 2, w.T - 1] + list(rng.integers(0, w.T, 10))))
+    kv64 = orc.bf16_to_f64(x["kv"])
+    s64 = x["sink"].astype(np.float64)
+    want = [orc.forward_token(orc.bf16_to_f64(x["q"][t]), kv64, x["idx"][t], s64, SCALE) for t in toks]
+    assert_close("O sampled", host_bf16(o[toks]), np.stack([wo for wo, _ in want]))
+    got = lse[toks].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got - np.stack([wl for _, wl in want]))) < 1e-4
+
+
 # ---------------------------------------------------------------------------
 # edge cases: ragged shapes, masks, empty inputs
 # ---------------------------------------------------------------------------
