@@ -265,6 +265,29 @@ def main():
                "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
                "note": "smla_fwd (O and lse) on the same inputs; nominal 4*T*H*topk*512 flops"}
 
+    # the bounded-workspace backward (token phases of 1024) on the same inputs
+    ph_tokens = 1024
+    ph_ws = torch.empty(B.lib().smla_bwd_phased_workspace_bytes(T, H, N, K, ph_tokens),
+                        dtype=torch.uint8, device="cuda")
+
+    def phased():
+        B.smla_bwd_phased(q, kv, dO, O, lse, idx, sink, scale, phase_tokens=ph_tokens, workspace=ph_ws,
+                          out=(dq2, dkv2, ds2))
+    phased()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.stage_steps):
+        phased()
+    b.record()
+    torch.cuda.synchronize()
+    ph_ms = a.elapsed_time(b) / args.stage_steps
+    phased_row = {"phase_tokens": ph_tokens, "ms": round(ph_ms, 4),
+                  "tflops": round(w.flops() / (ph_ms * 1e-3) / 1e12, 1),
+                  "workspace_gib": round(ph_ws.numel() / 2 ** 30, 3),
+                  "full_workspace_gib": round(ws.numel() / 2 ** 30, 3)}
+    del ph_ws
+
     cpu = None
     if args.cpu_baseline == "on":
         print(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr,
@@ -294,6 +317,7 @@ def main():
                    "valid_slots": nnz},
         "stages": stage_rows,
         "forward": forward,
+        "phased": phased_row,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "context": {"pages_own_backward_mi355x": {"ms": 3.238, "tflops": 424},

@@ -120,6 +120,29 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
              uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of workspace smla_bwd_phased needs (0 on a shape error or phase_tokens < 1). */
+size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int phase_tokens);
+
+/*
+ * smla_bwd_phased -- the same backward with a workspace bounded by a token
+ * phase instead of T.  The page notes that the intermediate grows as
+ * T * topk * 512 bf16 (its R_CHUNK note, Structure section); here the dS/P
+ * blocks, the intermediate, the inverted index and the gather scratch hold
+ * phase_tokens tokens at a time, and dkv is carried across phases as an fp32
+ * running sum (num_kv * 2 KiB of workspace) that is rounded to bf16 once.
+ *   phase_tokens >= 1 (else SMLA_ERR_SHAPE); all other arguments as smla_bwd.
+ * Phases run in token order; each phase's inverted index is built on the
+ * helper stream while dQ and the intermediate of that phase run (the same
+ * fork/join pattern as smla_bwd).  With
+ * phase_tokens >= T the results equal smla_bwd's bit for bit; otherwise dkv
+ * differs from it only by the fp32 summation order across phases.
+ */
+int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+                    const float* lse, const int32_t* idx, const float* sink, const float* dlse,
+                    int T, int H, int num_kv, int topk, float scale, int phase_tokens,
+                    uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* The backward's stages, exported individually (same conventions)          */
 /* ------------------------------------------------------------------------ */

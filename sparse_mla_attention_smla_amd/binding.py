@@ -5,8 +5,8 @@ stream -> a stream handle, C status codes -> exceptions.  Every computation runs
 in the library's HIP kernels; there is no fallback path.  If the library is
 missing, every call raises.
 
-Function names follow the C entry points: smla_fwd, smla_bwd, smla_delta,
-smla_dq, smla_interm, smla_build_csr, smla_gather, smla_dsink.
+Function names follow the C entry points: smla_fwd, smla_bwd, smla_bwd_phased,
+smla_delta, smla_dq, smla_interm, smla_build_csr, smla_gather, smla_dsink.
 """
 from __future__ import annotations
 
@@ -34,6 +34,9 @@ _SIGNATURES = {
     "smla_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "smla_bwd_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "smla_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "smla_bwd_phased_workspace_bytes": ([_I, _I, _I, _I, _I], _Z),
+    "smla_bwd_phased": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _Z,
+                         _P], _I),
     "smla_delta": ([_P, _P, _P, _I, _I, _P, _P], _I),
     "smla_dq": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "smla_interm": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
@@ -182,6 +185,43 @@ def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=
     _check("smla_bwd", lib().smla_bwd(
         _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
         _default_scale(scale), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
+        _ptr(workspace), workspace.numel(), _stream(q.device)))
+    if count_invalid:
+        return dq, dkv, d_sink, n_inv
+    return dq, dkv, d_sink
+
+
+def smla_bwd_phased(q, kv, dO, o, lse, idx, sink=None, scale=None, phase_tokens=1024, workspace=None,
+                    out=None, count_invalid=False, dlse=None):
+    """The backward with a workspace bounded by `phase_tokens` tokens: returns
+    (dq, dkv, d_sink[, n_invalid]) like smla_bwd."""
+    T, H, _ = q.shape
+    N, K = kv.shape[0], idx.shape[1]
+    _need(q, "q", torch.bfloat16, (T, H, D))
+    _need(kv, "kv", torch.bfloat16, (N, D))
+    _need(dO, "dO", torch.bfloat16, (T, H, D))
+    _need(o, "o", torch.bfloat16, (T, H, D))
+    _need(lse, "lse", torch.float32, (T, H))
+    _need(idx, "idx", torch.int32, (T, K))
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (H,))
+    if dlse is not None:
+        _need(dlse, "dlse", torch.float32, (T, H))
+    if out is None:
+        dq = torch.empty_like(q)
+        dkv = torch.empty_like(kv)
+        d_sink = torch.empty((H,), dtype=torch.float32, device=q.device) if sink is not None else None
+    else:
+        dq, dkv, d_sink = out
+    if workspace is None:
+        n = lib().smla_bwd_phased_workspace_bytes(T, H, N, K, int(phase_tokens))
+        if n == 0:
+            raise SmlaError("smla_bwd_phased_workspace_bytes", 2)
+        workspace = torch.empty((n,), dtype=torch.uint8, device=q.device)
+    n_inv = torch.empty((1,), dtype=torch.int32, device=q.device) if count_invalid else None
+    _check("smla_bwd_phased", lib().smla_bwd_phased(
+        _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
+        _default_scale(scale), int(phase_tokens), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
         _ptr(workspace), workspace.numel(), _stream(q.device)))
     if count_invalid:
         return dq, dkv, d_sink, n_inv

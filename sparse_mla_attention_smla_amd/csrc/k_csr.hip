@@ -222,6 +222,20 @@ __global__ __launch_bounds__(kSortThreads) void smla_k4_csr_scatter(
     }
 }
 
+// out = sum of n per-call counts, in index order (one wave)
+__global__ __launch_bounds__(64) void smla_k4_sum_counts(const int32_t* __restrict__ c, int n,
+                                                         int32_t* __restrict__ out) {
+    int s = 0;
+    for (int i = threadIdx.x; i < n; i += 64) s += c[i];
+    for (int m = 32; m > 0; m >>= 1) s += wave_xor(s, m);
+    if (threadIdx.x == 0) *out = s;
+}
+
+hipError_t launch_sum_counts(const int32_t* counts, int n, int32_t* out, hipStream_t s) {
+    smla_k4_sum_counts<<<1, 64, 0, s>>>(counts, n, out);
+    return hipGetLastError();
+}
+
 size_t csr_scratch_bytes(int64_t M, int N) {
     const int64_t nblk = csr_blocks(M);
     return align_up((size_t)M * 4, 256) + align_up((size_t)nblk * N * 4, 256) +

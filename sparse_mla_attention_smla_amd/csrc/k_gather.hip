@@ -139,6 +139,45 @@ __global__ __launch_bounds__(256) void smla_k5_gather_combine(const float* __res
     *reinterpret_cast<u32x4*>(dkv + (size_t)j * kD + lane * 8) = out;
 }
 
+// Token-phased variant of the combine: the row's segment partials of this
+// phase are added, in order, to its fp32 running sum (started at zero in the
+// first phase); the last phase rounds the sum to bf16 once.  With a single
+// phase this is the plain combine, operation for operation.
+__global__ __launch_bounds__(256) void smla_k5_gather_combine_acc(const float* __restrict__ partial,
+                                                                  const int32_t* __restrict__ seg_ptr,
+                                                                  int N, int first,
+                                                                  float* __restrict__ run,
+                                                                  uint16_t* __restrict__ dkv) {
+    const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (j >= N) return;
+    const int s0 = seg_ptr[j], s1 = seg_ptr[j + 1];
+    f32x4* r = reinterpret_cast<f32x4*>(run + (size_t)j * kD + lane * 8);
+    float acc[8];
+    if (first) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    } else {
+        const f32x4 a = r[0], b = r[1];
+        acc[0] = a[0]; acc[1] = a[1]; acc[2] = a[2]; acc[3] = a[3];
+        acc[4] = b[0]; acc[5] = b[1]; acc[6] = b[2]; acc[7] = b[3];
+    }
+    for (int s = s0; s < s1; ++s) {
+        const f32x4* p = reinterpret_cast<const f32x4*>(partial + (size_t)s * kD + lane * 8);
+        const f32x4 a = p[0], b = p[1];
+        acc[0] += a[0]; acc[1] += a[1]; acc[2] += a[2]; acc[3] += a[3];
+        acc[4] += b[0]; acc[5] += b[1]; acc[6] += b[2]; acc[7] += b[3];
+    }
+    if (dkv != nullptr) {
+        u32x4 out = {pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3]), pack_bf16(acc[4], acc[5]),
+                     pack_bf16(acc[6], acc[7])};
+        *reinterpret_cast<u32x4*>(dkv + (size_t)j * kD + lane * 8) = out;
+    } else {
+        r[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+        r[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+}
+
 size_t gather_scratch_bytes(int64_t M, int N) {
     const int64_t ms = gather_max_segments(M, N);
     return align_up((size_t)(N + 1) * 4, 256) + align_up((size_t)ms * 4, 256) +
@@ -171,6 +210,18 @@ hipError_t launch_gather_sum(const uint16_t* interm, const int32_t* row_ptr, con
                                                                    ws.seg_ptr, ws.seg_row, N, M,
                                                                    ws.partial);
     smla_k5_gather_combine<<<(N + 3) / 4, 256, 0, s>>>(ws.partial, ws.seg_ptr, N, dkv);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_sum_phase(const uint16_t* interm, const int32_t* row_ptr,
+                                   const int32_t* slots, int64_t M, int N, const GatherScratch& ws,
+                                   bool first, float* run, uint16_t* dkv_last, hipStream_t s) {
+    const int64_t ms = gather_max_segments(M, N);
+    smla_k5_gather_segment<<<(unsigned)ms, kSegWaves * 64, 0, s>>>(interm, row_ptr, slots,
+                                                                   ws.seg_ptr, ws.seg_row, N, M,
+                                                                   ws.partial);
+    smla_k5_gather_combine_acc<<<(N + 3) / 4, 256, 0, s>>>(ws.partial, ws.seg_ptr, N, first ? 1 : 0,
+                                                           run, dkv_last);
     return hipGetLastError();
 }
 

@@ -63,12 +63,13 @@ namespace {
 // A helper stream per device (default priority, non-blocking) with fork, join
 // and after-delta events: smla_bwd runs the CSR build, the gather plan and
 // (once delta is done) d_sink there, concurrently with delta, dQ and the
-// intermediate, and joins before the gather sums.  One mutex covers a
-// whole smla_bwd enqueue so calls from several host threads cannot interleave
-// records of the shared events.
+// intermediate, and joins before the gather sums (smla_bwd_phased does the
+// same per token phase).  One mutex covers a whole enqueue so calls from
+// several host threads cannot interleave records of the shared events.
 struct SideStream {
     hipStream_t s = nullptr;
     hipEvent_t fork = nullptr, join = nullptr, after_delta = nullptr;
+    hipEvent_t gather_done = nullptr;   // phased backward: the phase's gather has read the CSR
     int state = 0;  // 0 not tried, 1 ready, 2 unavailable
 };
 SideStream g_side[kMaxDevices];
@@ -81,7 +82,8 @@ SideStream* side_stream(int dev) {
         if (hipStreamCreateWithFlags(&d.s, hipStreamNonBlocking) == hipSuccess &&
             hipEventCreateWithFlags(&d.fork, hipEventDisableTiming) == hipSuccess &&
             hipEventCreateWithFlags(&d.join, hipEventDisableTiming) == hipSuccess &&
-            hipEventCreateWithFlags(&d.after_delta, hipEventDisableTiming) == hipSuccess)
+            hipEventCreateWithFlags(&d.after_delta, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&d.gather_done, hipEventDisableTiming) == hipSuccess)
             d.state = 1;
     }
     return d.state == 1 ? &d : nullptr;
@@ -149,6 +151,41 @@ BwdLayout bwd_layout(int T, int H, int num_kv, int topk) {
     return L;
 }
 
+// Token-phased backward: phases of Tp = min(phase_tokens, T) tokens (at least
+// one phase); the dS/P blocks, the intermediate, the CSR and the gather scratch
+// are sized for one phase, plus an fp32 running dkv and one invalid-index count
+// per phase.
+struct PhasedLayout {
+    int Tp, nphase;
+    size_t delta, dsp, interm, row_ptr, slots, csr, gather, dsink, run, inv, total;
+};
+
+PhasedLayout phased_layout(int T, int H, int num_kv, int topk, int phase_tokens) {
+    PhasedLayout L;
+    L.Tp = T < phase_tokens ? T : phase_tokens;
+    if (L.Tp < 1) L.Tp = 1;
+    L.nphase = T > 0 ? (T + L.Tp - 1) / L.Tp : 1;
+    const int64_t Mp = (int64_t)L.Tp * topk;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align_up(bytes, kWsAlign);
+        return at;
+    };
+    L.delta = take((size_t)T * H * 4);
+    L.dsp = take(dsp_bytes(L.Tp, H, topk));
+    L.interm = take((size_t)Mp * kD * 2);
+    L.row_ptr = take((size_t)(num_kv + 1) * 4);
+    L.slots = take((size_t)Mp * 4);
+    L.csr = take(csr_scratch_bytes(Mp, num_kv));
+    L.gather = take(gather_scratch_bytes(Mp, num_kv));
+    L.dsink = take((size_t)(dsink_blocks(T) > 0 ? dsink_blocks(T) : 1) * H * 4);
+    L.run = take((size_t)num_kv * kD * 4);
+    L.inv = take((size_t)L.nphase * 4);
+    L.total = off;
+    return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,6 +206,11 @@ const char* smla_status_string(int status) {
 size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk) {
     if (check_shape(T, H, num_kv, topk) != SMLA_OK) return 0;
     return bwd_layout(T, H, num_kv, topk).total;
+}
+
+size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int phase_tokens) {
+    if (check_shape(T, H, num_kv, topk) != SMLA_OK || phase_tokens < 1) return 0;
+    return phased_layout(T, H, num_kv, topk, phase_tokens).total;
 }
 
 size_t smla_csr_workspace_bytes(int T, int topk, int num_kv) {
@@ -289,6 +331,108 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
         return SMLA_ERR_HIP;
     if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SMLA_ERR_HIP;
     if (launch_gather_sum(interm, row_ptr, slots, M, num_kv, gs, dkv, s) != hipSuccess)
+        return SMLA_ERR_HIP;
+    return SMLA_OK;
+}
+
+int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+                    const float* lse, const int32_t* idx, const float* sink, const float* dlse,
+                    int T, int H, int num_kv, int topk, float scale, int phase_tokens, uint16_t* dq,
+                    uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    smla_status st = check_shape(T, H, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    if (phase_tokens < 1) return SMLA_ERR_SHAPE;
+    if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+    if (!kv || !dkv) return SMLA_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !dO || !o || !lse || !idx || !dq)) return SMLA_ERR_INVALID_ARG;
+    if ((sink == nullptr) != (d_sink == nullptr)) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(dO, 16) || !aligned(o, 16) ||
+        !aligned(dq, 16) || !aligned(dkv, 16) || !aligned(lse, 4) || !aligned(idx, 4) ||
+        !aligned(sink, 4) || !aligned(dlse, 4) || !aligned(d_sink, 4) ||
+        !aligned(n_invalid, 4) || !aligned(workspace, 16))
+        return SMLA_ERR_ALIGN;
+    const PhasedLayout L = phased_layout(T, H, num_kv, topk, phase_tokens);
+    if (workspace == nullptr || workspace_bytes < L.total) return SMLA_ERR_WORKSPACE;
+    const size_t qb = (size_t)T * H * kD * 2;
+    const size_t hb = (size_t)H * 4;
+    const Range all[] = {{q, qb},
+                         {kv, (size_t)num_kv * kD * 2},
+                         {dO, qb},
+                         {o, qb},
+                         {lse, (size_t)T * H * 4},
+                         {idx, (size_t)T * topk * 4},
+                         {sink, sink ? hb : 0},
+                         {dlse, dlse ? (size_t)T * H * 4 : 0},
+                         {dq, qb},
+                         {dkv, (size_t)num_kv * kD * 2},
+                         {d_sink, d_sink ? hb : 0},
+                         {n_invalid, n_invalid ? 4u : 0u},
+                         {workspace, L.total}};
+    if (!outputs_disjoint(all, 13, 8)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    float* delta = reinterpret_cast<float*>(ws + L.delta);
+    uint16_t* dsp = reinterpret_cast<uint16_t*>(ws + L.dsp);
+    uint16_t* interm = reinterpret_cast<uint16_t*>(ws + L.interm);
+    int32_t* row_ptr = reinterpret_cast<int32_t*>(ws + L.row_ptr);
+    int32_t* slots = reinterpret_cast<int32_t*>(ws + L.slots);
+    const int64_t Mp = (int64_t)L.Tp * topk;
+    const CsrScratch cs = csr_carve(ws + L.csr, Mp, num_kv);
+    const GatherScratch gs = gather_carve(ws + L.gather, Mp, num_kv);
+    float* dsink_part = reinterpret_cast<float*>(ws + L.dsink);
+    float* run = reinterpret_cast<float*>(ws + L.run);
+    int32_t* inv = reinterpret_cast<int32_t*>(ws + L.inv);
+
+    // delta and d_sink cover all tokens at once; every later stage runs per
+    // phase on token-range views, in phase order.  As in smla_bwd, the inverted
+    // index and gather plan of a phase are built on the helper stream while dQ
+    // and the intermediate of that phase run on the caller's stream; the next
+    // phase's build waits until this phase's gather has read them.
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    SideStream* side = side_stream(dev);
+    hipStream_t aux = side != nullptr ? side->s : s;
+    auto rec_wait = [&](hipEvent_t e, hipStream_t from, hipStream_t to) {
+        return side == nullptr ||
+               (hipEventRecord(e, from) == hipSuccess && hipStreamWaitEvent(to, e, 0) == hipSuccess);
+    };
+    if (!rec_wait(side ? side->fork : nullptr, s, aux)) return SMLA_ERR_HIP;
+    if (launch_delta(o, dO, dlse, (int64_t)T * H, delta, s) != hipSuccess) return SMLA_ERR_HIP;
+    for (int p = 0; p < L.nphase; ++p) {
+        const int t0 = p * L.Tp;
+        const int tp = T - t0 < L.Tp ? T - t0 : L.Tp;
+        const size_t tok = (size_t)t0 * H * kD;
+        const size_t row = (size_t)t0 * H;
+        const int32_t* idx_p = idx + (size_t)t0 * topk;
+        const int64_t M = (int64_t)tp * topk;
+        if (p > 0 && !rec_wait(side ? side->gather_done : nullptr, s, aux)) return SMLA_ERR_HIP;
+        if (launch_csr(idx_p, M, num_kv, cs, row_ptr, slots, n_invalid ? inv + p : nullptr, aux) !=
+            hipSuccess)
+            return SMLA_ERR_HIP;
+        if (launch_gather_plan(row_ptr, M, num_kv, gs, aux) != hipSuccess) return SMLA_ERR_HIP;
+        if (side != nullptr && hipEventRecord(side->join, aux) != hipSuccess) return SMLA_ERR_HIP;
+        if (p == 0 && sink != nullptr) {
+            if (!rec_wait(side ? side->after_delta : nullptr, s, aux)) return SMLA_ERR_HIP;
+            if (launch_dsink(lse, delta, sink, T, H, dsink_part, d_sink, aux) != hipSuccess)
+                return SMLA_ERR_HIP;
+        }
+        if (launch_dq(q + tok, kv, dO + tok, lse + row, delta + row, idx_p, tp, H, num_kv, topk, scale,
+                      dq + tok, dsp, s) != hipSuccess)
+            return SMLA_ERR_HIP;
+        if (launch_interm(q + tok, dO + tok, dsp, idx_p, tp, H, num_kv, topk, interm, s) != hipSuccess)
+            return SMLA_ERR_HIP;
+        if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SMLA_ERR_HIP;
+        if (launch_gather_sum_phase(interm, row_ptr, slots, M, num_kv, gs, p == 0, run,
+                                    p + 1 == L.nphase ? dkv : nullptr, s) != hipSuccess)
+            return SMLA_ERR_HIP;
+    }
+    // everything enqueued on the helper stream (d_sink included) joins here
+    if (!rec_wait(side ? side->join : nullptr, aux, s)) return SMLA_ERR_HIP;
+    if (n_invalid != nullptr && launch_sum_counts(inv, L.nphase, n_invalid, s) != hipSuccess)
         return SMLA_ERR_HIP;
     return SMLA_OK;
 }

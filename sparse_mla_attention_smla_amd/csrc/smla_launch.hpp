@@ -33,6 +33,8 @@ size_t csr_scratch_bytes(int64_t M, int N);
 CsrScratch csr_carve(void* base, int64_t M, int N);
 hipError_t launch_csr(const int32_t* idx, int64_t M, int N, const CsrScratch& ws, int32_t* row_ptr,
                       int32_t* slots, int32_t* n_invalid, hipStream_t s);
+// *out = counts[0] + ... + counts[n-1]
+hipError_t launch_sum_counts(const int32_t* counts, int n, int32_t* out, hipStream_t s);
 
 // ---- gather ---------------------------------------------------------------
 constexpr int kGatherSeg = 128;  // contributors per gather segment
@@ -52,6 +54,12 @@ hipError_t launch_gather_sum(const uint16_t* interm, const int32_t* row_ptr, con
                              int64_t M, int N, const GatherScratch& ws, uint16_t* dkv, hipStream_t s);
 hipError_t launch_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* slots,
                          int64_t M, int N, const GatherScratch& ws, uint16_t* dkv, hipStream_t s);
+// one token phase of a phased backward: adds the phase's sums to the fp32
+// running sums `run` [N, 512] (set, when first); dkv_last (non-null on the
+// last phase only) receives the bf16 rounding of the final sums instead
+hipError_t launch_gather_sum_phase(const uint16_t* interm, const int32_t* row_ptr,
+                                   const int32_t* slots, int64_t M, int N, const GatherScratch& ws,
+                                   bool first, float* run, uint16_t* dkv_last, hipStream_t s);
 
 // ---- attention tiles (MFMA) -----------------------------------------------
 hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const float* lse,

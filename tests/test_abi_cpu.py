@@ -34,7 +34,7 @@ def lib():
 
 def test_header_and_binding_agree(lib):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     assert sorted(B.EXPORTED) == names
 
 
@@ -61,6 +61,12 @@ def test_workspace_sizes(lib):
     assert lib.smla_csr_workspace_bytes(64, 16, 64) > 0
     assert lib.smla_gather_workspace_bytes(64, 16, 64) > 0
     assert lib.smla_dsink_workspace_bytes(64, 16) == 2 * 16 * 4
+    # phased: bounded by the phase, plus an fp32 running dkv (num_kv * 2 KiB)
+    full = lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 4096)
+    part = lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 512)
+    assert part < full / 6 and full > n
+    assert lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 10 ** 6) == full
+    assert lib.smla_bwd_phased_workspace_bytes(64, 16, 64, 16, 0) == 0
 
 
 A = 0x10000000  # fake, 256-B aligned device addresses (never dereferenced)
@@ -97,6 +103,22 @@ def test_bwd_argument_errors(lib):
     assert _bwd(lib, dlse=12 * A) in (HIP, ARCH)          # dlse is optional
     # a valid call gets past validation and then needs a gfx950 device
     assert _bwd(lib) in (HIP, ARCH)
+
+
+def test_phased_argument_errors(lib):
+    def call(phase=16, ws=1 << 34, **kw):
+        p = dict(q=A, kv=2 * A, dO=3 * A, o=4 * A, lse=5 * A, idx=6 * A, sink=7 * A, dlse=None,
+                 dq=8 * A, dkv=9 * A, d_sink=10 * A, n_inv=None, work=11 * A)
+        p.update(kw)
+        return lib.smla_bwd_phased(p["q"], p["kv"], p["dO"], p["o"], p["lse"], p["idx"], p["sink"],
+                                   p["dlse"], 64, 16, 64, 16, 0.05, phase, p["dq"], p["dkv"],
+                                   p["d_sink"], p["n_inv"], p["work"], ws, None)
+    assert call(phase=0) == SHAPE
+    assert call(ws=1024) == WORKSPACE
+    assert call(d_sink=None) == INVALID
+    assert call(dkv=A) == INVALID                          # dkv aliases q
+    assert call(dlse=12 * A + 2) == ALIGN
+    assert call() in (HIP, ARCH)
 
 
 def test_stage_argument_errors(lib):

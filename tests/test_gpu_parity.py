@@ -430,6 +430,118 @@ def test_error_codes_from_device_side_entry():
 
 
 # ---------------------------------------------------------------------------
+# token-phased backward (bounded workspace)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,phase,with_dlse", [("small", 100, False), ("small_nosink", 300, True),
+                                                  ("tiny", 7, True)])
+def test_phased_matches_oracle(name, phase, with_dlse):
+    x = workload_nosink("small") if name == "small_nosink" else workload(name)
+    base = name.replace("_nosink", "")
+    dlse = inputs.make_dlse(base) if with_dlse else None
+    _say(f"[phased] {name} phase_tokens={phase} dlse={with_dlse}")
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, dlse=dlse)
+    d = _to_dev(x)
+    dq, dkv, ds, n_inv = B.smla_bwd_phased(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"],
+                                           SCALE, phase_tokens=phase, count_invalid=True,
+                                           dlse=None if dlse is None else dev(dlse))
+    torch.cuda.synchronize()
+    assert_close(f"{name} dq (phased)", host_bf16(dq), ref["dq"])
+    assert_close(f"{name} dkv (phased)", host_bf16(dkv), ref["dkv"])
+    if x["sink"] is not None:
+        assert_close(f"{name} d_sink (phased)", ds.cpu().numpy(), ref["d_sink"])
+    assert int(n_inv.item()) == 0
+
+
+def test_phased_one_phase_equals_bwd():
+    x = workload("small")
+    d = _to_dev(x)
+    T = x["q"].shape[0]
+    a = _run_bwd(d)
+    for phase in (T, 10 * T):
+        b = B.smla_bwd_phased(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"], SCALE,
+                              phase_tokens=phase)
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(host_bits_t(a[i]), host_bits_t(b[i])), (phase, i)
+        assert torch.equal(a[2], b[2])
+
+
+def test_phased_graph_capture_replays_match_eager():
+    """The phased backward forks to the helper stream once per phase; captured
+    into a graph, every replay must equal the eager call bit for bit."""
+    x = workload("small")
+    d = _to_dev(x)
+    T, H, _ = x["q"].shape
+    N, K = x["kv"].shape[0], x["idx"].shape[1]
+    ws = torch.empty((B.lib().smla_bwd_phased_workspace_bytes(T, H, N, K, 300),), dtype=torch.uint8,
+                     device="cuda")
+    args = (d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"], SCALE)
+    eager = B.smla_bwd_phased(*args, phase_tokens=300, workspace=ws)
+    torch.cuda.synchronize()
+    dq, dkv, ds = torch.empty_like(d["q"]), torch.empty_like(d["kv"]), torch.empty_like(d["sink"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.smla_bwd_phased(*args, phase_tokens=300, workspace=ws, out=(dq, dkv, ds))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.smla_bwd_phased(*args, phase_tokens=300, workspace=ws, out=(dq, dkv, ds))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dq.fill_(0); dkv.fill_(0); ds.fill_(0); ws.fill_(0x33)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(host_bits_t(dq), host_bits_t(eager[0])), f"replay {rep}: dq"
+        assert torch.equal(host_bits_t(dkv), host_bits_t(eager[1])), f"replay {rep}: dkv"
+        assert torch.equal(ds, eager[2]), f"replay {rep}: d_sink"
+
+
+def test_phased_invalid_indices_are_counted_over_phases():
+    x = dict(workload("small"))
+    rng = np.random.default_rng(12)
+    idx = x["idx"].copy()
+    bad = rng.random(idx.shape) < 0.02
+    idx = np.where(bad, np.where(rng.random(idx.shape) < 0.5, -9, x["kv"].shape[0] + 1), idx).astype(np.int32)
+    x["idx"] = idx
+    x = _oracle_inputs(x)
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], idx, x["sink"], SCALE)
+    d = _to_dev(x)
+    dq, dkv, ds, n_inv = B.smla_bwd_phased(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"],
+                                           SCALE, phase_tokens=333, count_invalid=True)
+    torch.cuda.synchronize()
+    assert_close("dq", host_bf16(dq), ref["dq"])
+    assert_close("dkv", host_bf16(dkv), ref["dkv"])
+    assert int(n_inv.item()) == orc.count_invalid(idx, x["kv"].shape[0]) > 0
+
+
+def test_phased_headline_sampled():
+    x = workload("headline")
+    w = x["workload"]
+    d = _to_dev(x)
+    _say("[phased] headline, phase_tokens=1000")
+    dq, dkv, ds = B.smla_bwd_phased(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"], SCALE,
+                                    phase_tokens=1000)
+    torch.cuda.synchronize()
+    toks = [0, 999, 1000, 2047, 3999, 4000, w.T - 1]
+    r = orc.backward_tokens(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, toks)
+    assert_close("headline dq (phased)", host_bf16(dq[toks]), r["dq"])
+    rp, _ = orc.csr(x["idx"], w.num_kv)
+    counts = np.diff(rp)
+    busiest = int(w.T + np.argmax(counts[w.T:]))
+    rows = [3, 998, 1500, w.T - 2, busiest]
+    want = orc.dkv_rows(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, rows)
+    assert_close("headline dkv (phased)", host_bf16(dkv[rows]), want)
+    assert_close("headline d_sink (phased)", ds.cpu().numpy(),
+                 orc.d_sink(x["dO"], x["O"], x["lse"], x["sink"]))
+    del d
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------
 # full-size workloads (the benchmark's launch configuration), sampled outputs
 # ---------------------------------------------------------------------------
 
