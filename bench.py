@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
+    ap.add_argument("--phased", choices=["on", "off"], default="off",
+                    help="also time the bounded-workspace backward (1024-token phases); its "
+                         "smaller dQ/intermediate launches would mix into a kernel trace")
     ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--stage-steps", type=int, default=10)
     ap.add_argument("--mode", choices=["full", "profile"], default="full",
@@ -75,6 +78,31 @@ def stored_traffic(kernel: str):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq, dkv, ds, reps):
+    """ms per call of the bounded-workspace backward on the same inputs and outputs."""
+    import torch
+    T, H, N, K = w.T, w.H, w.num_kv, w.topk
+    ph_ws = torch.empty(B.lib().smla_bwd_phased_workspace_bytes(T, H, N, K, ph_tokens),
+                        dtype=torch.uint8, device="cuda")
+
+    def phased():
+        B.smla_bwd_phased(q, kv, dO, O, lse, idx, sink, scale, phase_tokens=ph_tokens, workspace=ph_ws,
+                          out=(dq, dkv, ds))
+    phased()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        phased()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return {"phase_tokens": ph_tokens, "ms": round(ms, 4),
+            "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 1),
+            "workspace_gib": round(ph_ws.numel() / 2 ** 30, 3),
+            "full_workspace_gib": round(ws.numel() / 2 ** 30, 3)}
 
 
 def cpu_baseline(w, n_tokens):
@@ -266,27 +294,11 @@ def main():
                "note": "smla_fwd (O and lse) on the same inputs; nominal 4*T*H*topk*512 flops"}
 
     # the bounded-workspace backward (token phases of 1024) on the same inputs
+    phased_row = None
     ph_tokens = 1024
-    ph_ws = torch.empty(B.lib().smla_bwd_phased_workspace_bytes(T, H, N, K, ph_tokens),
-                        dtype=torch.uint8, device="cuda")
-
-    def phased():
-        B.smla_bwd_phased(q, kv, dO, O, lse, idx, sink, scale, phase_tokens=ph_tokens, workspace=ph_ws,
-                          out=(dq2, dkv2, ds2))
-    phased()
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(args.stage_steps):
-        phased()
-    b.record()
-    torch.cuda.synchronize()
-    ph_ms = a.elapsed_time(b) / args.stage_steps
-    phased_row = {"phase_tokens": ph_tokens, "ms": round(ph_ms, 4),
-                  "tflops": round(w.flops() / (ph_ms * 1e-3) / 1e12, 1),
-                  "workspace_gib": round(ph_ws.numel() / 2 ** 30, 3),
-                  "full_workspace_gib": round(ws.numel() / 2 ** 30, 3)}
-    del ph_ws
+    if args.phased == "on":
+        phased_row = time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq2, dkv2,
+                                 ds2, args.stage_steps)
 
     cpu = None
     if args.cpu_baseline == "on":
