@@ -211,7 +211,7 @@ struct ItemSeq {
 // Producers run one tile ahead of consumers; one barrier per tile.  The tiles
 // of consecutive segments form one stream over the 4-deep ring: while segment
 // s ends, the first tiles of segment s+1 are already copied, its slot list
-// (double-buffered, built by wave 4 during segment s) is ready, its first tile
+// (double-buffered, built by producer 0 during segment s) is ready, its first tile
 // is produced, and for a new item the producers reload q and dO during their
 // last tile of the old one.  Segments shorter than kMinStream tiles end with a
 // drain and restart instead.
@@ -334,6 +334,10 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         }
     };
     auto finish_load = [&]() {
+        // keep the lane permutation (and the wait for the loads it implies) after
+        // everything before it: hoisted into a reload tile's MFMA loop it would
+        // stall that loop on the loads' latency
+        __builtin_amdgcn_sched_barrier(0);
         frag_to_mfma_lanes(qf, lane);
         if constexpr (!FWD) frag_to_mfma_lanes(dof, lane);
         settle_scalars(nbias, ndl);
@@ -575,7 +579,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     }
     __syncthreads();
 
-    SlotChunk nxt;     // wave 4: index slots of the next segment, loaded early
+    SlotChunk nxt;     // producer 0: index slots of the next segment, loaded early
     int base = 0;      // stream position of tile 0 of segment s
     bool primed = false;
     int post_epi = 0;  // consumer: iterations whose wait must skip the last epilogue's stores
@@ -629,6 +633,12 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             }
             __syncthreads();
             if constexpr (PROD) {
+                // producer 0 builds the next segment's slot list: its index loads,
+                // issued a tile early, are waited for by compiler-counted stores only
+                if (w == 0 && has_next && ntile >= 2) {
+                    if (j == 0) load_slot_chunk(idx_next, K, k0_next, nxt, lane);
+                    else if (j == 1) build_slot_list(nxt, N, k0_next, &Lb[(s + 1) & 1], lane);
+                }
                 if (j + 1 < ntile) {
                     if (j + 2 == ntile && cont && next_new_item) {
                         int h; size_t lrow;
@@ -652,8 +662,6 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                     if (p_n > 0) produce(pos + 1, 0, NoReload{}, nullptr, nullptr);
                 }
             } else {
-                if (w == 4 && has_next && ntile >= 2 && j == 1)
-                    build_slot_list(nxt, N, k0_next, &Lb[(s + 1) & 1], lane);
                 const int ahead = j + kNBuf - 1;
                 if (ahead < ntile || !cont) issue(&Lb[s & 1], ahead, pos + kNBuf - 1);
                 else issue(&Lb[(s + 1) & 1], ahead - ntile, pos + kNBuf - 1);
@@ -669,7 +677,6 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                     epilogue(item, pos);
                     post_epi = 2;
                 }
-                if (w == 4 && has_next && ntile >= 2 && j == 0) load_slot_chunk(idx_next, K, k0_next, nxt, lane);
             }
         }
         if (!cont) {
