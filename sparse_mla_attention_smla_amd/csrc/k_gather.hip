@@ -21,7 +21,9 @@
 namespace smla {
 
 namespace {
-constexpr int kSegWaves = 4;
+constexpr int kSegWaves = 16;
+static_assert(kGatherSeg % kSegWaves == 0 && kGatherSeg / kSegWaves <= 64,
+              "a wave's contributor slots fit one per lane");
 
 __device__ int block_exclusive_scan_1024_g(int v, int* lds, int* total) {
     const int tid = threadIdx.x;
@@ -80,7 +82,7 @@ __global__ __launch_bounds__(kSegWaves * 64) void smla_k5_gather_segment(
     const int beg = row_ptr[j] + (s - seg_ptr[j]) * kGatherSeg;  // plan checked the row's pointers
     const int end = min(beg + kGatherSeg, row_ptr[j + 1]);
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    // wave w owns contributors beg + w + kSegWaves*m, m < kGatherSeg/kSegWaves (<= 32)
+    // wave w owns contributors beg + w + kSegWaves*m, m < kGatherSeg/kSegWaves (<= 64)
     const int mine = beg + w + kSegWaves * lane;
     const int my_slot = (lane < kGatherSeg / kSegWaves && mine < end) ? slots[mine] : 0;
     const int n = (end - beg - w + kSegWaves - 1) / kSegWaves;  // contributors of this wave

@@ -37,7 +37,7 @@ hipError_t launch_csr(const int32_t* idx, int64_t M, int N, const CsrScratch& ws
 hipError_t launch_sum_counts(const int32_t* counts, int n, int32_t* out, hipStream_t s);
 
 // ---- gather ---------------------------------------------------------------
-constexpr int kGatherSeg = 128;  // contributors per gather segment
+constexpr int kGatherSeg = 1024;  // contributors per gather segment (64 per wave of 16)
 inline int64_t gather_max_segments(int64_t M, int N) { return N + (M + kGatherSeg - 1) / kGatherSeg; }
 struct GatherScratch {
     int32_t* seg_ptr;   // [N + 1]
