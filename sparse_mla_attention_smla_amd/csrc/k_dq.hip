@@ -15,6 +15,9 @@
 // The S^T accumulator leaves each lane with one head and 8 slots, which is
 // exactly the B-operand layout of the second product: no data exchange.
 //
+// The persistent variant below also runs the forward (smla_k7_fwd_pc): the same
+// stream and roles, with an online softmax in place of the gradient.
+//
 // dsp layout (consumed by the intermediate kernel): for token t and compacted
 // tile c (c < ceil(topk/32)), a [2H][32] bf16 block at ((t*ceil(topk/32) + c)*2H)*32:
 // rows 0..H-1 hold scale*dS of head h, rows H..2H-1 hold P, column j is the
@@ -207,7 +210,8 @@ struct ItemSeq {
 //     fragment, published in LDS;
 //   consumers (waves 4-7): all 64 heads x 128 d of the dq accumulator each
 //     (every transposed kv read feeds four MFMAs); they also issue every kv
-//     row copy, so all explicit vmcnt waits count copies only.
+//     row copy, so each explicit vmcnt wait counts only that wave's own copies,
+//     warming copies and dq stores.
 // Producers run one tile ahead of consumers; one barrier per tile.  The tiles
 // of consecutive segments form one stream over the 4-deep ring: while segment
 // s ends, the first tiles of segment s+1 are already copied, its slot list
