@@ -20,6 +20,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -53,14 +54,23 @@ def parse():
 COPY_BYTES = 1 << 30
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and with whitespace collapsed (the sources
+    hold no string literal that contains a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: a stored HBM-traffic figure is only valid for these."""
+    """Hash of the HIP sources, comments and layout aside: a stored HBM-traffic
+    figure is only valid for this code."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_mla_attention_smla_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
         if f.endswith((".hip", ".hpp", ".cpp")):
             h.update(f.encode())
-            h.update(open(os.path.join(csrc, f), "rb").read())
+            h.update(_code_only(open(os.path.join(csrc, f)).read()).encode())
     return h.hexdigest()[:16]
 
 
