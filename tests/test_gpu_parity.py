@@ -373,6 +373,37 @@ def test_ragged_shapes(T, H, N, K, sink, with_dlse):
         assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
 
 
+@pytest.mark.parametrize("H,sink", [(64, True), (128, False)])
+def test_topk_beyond_one_chunk(H, sink):
+    """topk > 512: each token's slots form several 512-slot segments (the last
+    one empty for most rows), so the persistent dQ stream continues an item
+    across segments, and the forward takes its multi-chunk kernel."""
+    T, N, K = 20, 700, 1100
+    x = _custom(T, H, N, K, seed=K + H, sink=sink, pool_frac=1.0)
+    x["idx"][4] = -1
+    x["idx"][5, :] = np.sort(np.random.default_rng(3).choice(N, K, replace=True)).astype(np.int32)
+    x = _oracle_inputs(x)
+    _say(f"[topk>512] T={T} H={H} N={N} K={K} sink={sink}; valid per row "
+         f"{np.sum((x['idx'] >= 0), axis=1).tolist()}")
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE)
+    d = _to_dev(x)
+    dq, dkv, ds = _run_bwd(d)
+    assert_close("dq", host_bf16(dq), ref["dq"])
+    assert_close("dkv", host_bf16(dkv), ref["dkv"])
+    assert np.all(host_bf16(dq)[4] == 0.0)
+    if sink:
+        assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
+    O64, _ = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    o, _ = B.smla_fwd(d["q"], d["kv"], d["idx"], d["sink"], SCALE)
+    torch.cuda.synchronize()
+    assert_close("O", host_bf16(o), O64)
+    dq2, dkv2, _ = B.smla_bwd_phased(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"],
+                                     SCALE, phase_tokens=7)
+    torch.cuda.synchronize()
+    assert_close("dq (phased)", host_bf16(dq2), ref["dq"])
+    assert_close("dkv (phased)", host_bf16(dkv2), ref["dkv"])
+
+
 def test_shuffled_slots_invalid_indices_and_padding():
     x = dict(workload("small"))
     idx = inputs.shuffle_slots(x["idx"], seed=5)
