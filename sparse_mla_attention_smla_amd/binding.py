@@ -145,8 +145,10 @@ _ws_cache: dict = {}
 
 
 def bwd_workspace(T, H, num_kv, topk, device):
-    """A cached workspace buffer for this shape and device."""
-    key = (T, H, num_kv, topk, str(device))
+    """A cached workspace buffer for this shape, device and current stream.  Calls
+    on one stream run in order and may share it; a call on another stream (say,
+    from another host thread) gets its own, so concurrent calls never share one."""
+    key = (T, H, num_kv, topk, str(device), torch.cuda.current_stream(device).cuda_stream)
     ws = _ws_cache.get(key)
     if ws is None:
         ws = torch.empty(bwd_workspace_bytes(T, H, num_kv, topk), dtype=torch.uint8, device=device)

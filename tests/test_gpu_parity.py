@@ -200,6 +200,39 @@ def test_deterministic_and_poisoned_workspace(small_case):
         assert torch.equal(a[2], b[2]) and torch.equal(a[2], c[2])
 
 
+def test_concurrent_calls_from_two_threads(small_case):
+    """Two host threads, each on its own stream, call smla_bwd at the same time
+    (the enqueues share the library's helper stream); both results must equal
+    the single-threaded ones bit for bit."""
+    import threading
+    name, x, ref, d = small_case
+    want = _run_bwd(d)
+    d2 = dict(d)
+    d2["dO"] = (d["dO"].float() * -0.5).bfloat16()
+    want2 = _run_bwd(d2)
+    out = {}
+
+    def work(key, dd):
+        st = torch.cuda.Stream()
+        with torch.cuda.stream(st):
+            for _ in range(3):
+                r = B.smla_bwd(dd["q"], dd["kv"], dd["dO"], dd["O"], dd["lse"], dd["idx"], dd["sink"], SCALE)
+            st.synchronize()
+        out[key] = r
+
+    th = [threading.Thread(target=work, args=(k, dd)) for k, dd in (("a", d), ("b", d2))]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join()
+    torch.cuda.synchronize()
+    for key, w in (("a", want), ("b", want2)):
+        for i in range(2):
+            assert torch.equal(host_bits_t(out[key][i]), host_bits_t(w[i])), (key, i)
+        if w[2] is not None:
+            assert torch.equal(out[key][2], w[2]), key
+
+
 def test_graph_capture_replays_match_eager(small_case):
     """smla_bwd (including its fork to the helper stream and the join back) is
     captured into a graph; every replay, with eager work and synchronisations in
