@@ -12,7 +12,9 @@
 //   segment -- one block per segment sums its contributors in fp32 (each wave a
 //              fixed residue class of contributors, waves combined in order);
 //   combine -- one wave per kv row adds its segment partials in order and
-//              rounds to bf16 once.  Rows without contributors get zeros.
+//              rounds to bf16 once.  Rows without contributors get zeros; a
+//              row with a single segment is rounded and written by the segment
+//              kernel itself (same arithmetic, no partial round trip).
 // Every index read from row_ptr / slots is range-checked, so an inconsistent
 // inverted index can give wrong sums but never an out-of-bounds access.
 #include "smla_device.hpp"
@@ -74,7 +76,8 @@ __global__ __launch_bounds__(1024) void smla_k5_gather_plan(const int32_t* __res
 __global__ __launch_bounds__(kSegWaves * 64) void smla_k5_gather_segment(
     const uint16_t* __restrict__ interm, const int32_t* __restrict__ row_ptr,
     const int32_t* __restrict__ slots, const int32_t* __restrict__ seg_ptr,
-    const int32_t* __restrict__ seg_row, int N, int64_t M, float* __restrict__ partial) {
+    const int32_t* __restrict__ seg_row, int N, int64_t M, float* __restrict__ partial,
+    uint16_t* __restrict__ dkv_single) {
     __shared__ float red[kSegWaves][kD];
     const int s = blockIdx.x;
     if (s >= seg_ptr[N]) return;  // grid is an upper bound on the segment count
@@ -115,6 +118,20 @@ __global__ __launch_bounds__(kSegWaves * 64) void smla_k5_gather_segment(
 #pragma unroll
     for (int e = 0; e < 8; ++e) red[w][lane * 8 + e] = acc[e];
     __syncthreads();
+    if (dkv_single != nullptr && seg_ptr[j + 1] - seg_ptr[j] == 1) {
+        // the row's only segment: round to bf16 here, exactly as the combine
+        // would (it starts from +0, which also turns a -0 sum into +0)
+        for (int c2 = threadIdx.x; c2 < kD / 2; c2 += kSegWaves * 64) {
+            float a = red[0][2 * c2], b = red[0][2 * c2 + 1];
+#pragma unroll
+            for (int i = 1; i < kSegWaves; ++i) {
+                a += red[i][2 * c2];
+                b += red[i][2 * c2 + 1];
+            }
+            reinterpret_cast<uint32_t*>(dkv_single + (size_t)j * kD)[c2] = pack_bf16(0.f + a, 0.f + b);
+        }
+        return;
+    }
     for (int col = threadIdx.x; col < kD; col += kSegWaves * 64) {
         float sum = red[0][col];
 #pragma unroll
@@ -123,6 +140,7 @@ __global__ __launch_bounds__(kSegWaves * 64) void smla_k5_gather_segment(
     }
 }
 
+// Rows with exactly one segment were written by the segment kernel.
 __global__ __launch_bounds__(256) void smla_k5_gather_combine(const float* __restrict__ partial,
                                                               const int32_t* __restrict__ seg_ptr,
                                                               int N, uint16_t* __restrict__ dkv) {
@@ -130,6 +148,7 @@ __global__ __launch_bounds__(256) void smla_k5_gather_combine(const float* __res
     const int lane = threadIdx.x & 63;
     if (j >= N) return;
     const int s0 = seg_ptr[j], s1 = seg_ptr[j + 1];   // plan clamps both to the segment count
+    if (s1 - s0 == 1) return;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
@@ -213,7 +232,7 @@ hipError_t launch_gather_sum(const uint16_t* interm, const int32_t* row_ptr, con
     const int64_t ms = gather_max_segments(M, N);
     smla_k5_gather_segment<<<(unsigned)ms, kSegWaves * 64, 0, s>>>(interm, row_ptr, slots,
                                                                    ws.seg_ptr, ws.seg_row, N, M,
-                                                                   ws.partial);
+                                                                   ws.partial, dkv);
     smla_k5_gather_combine<<<(N + 3) / 4, 256, 0, s>>>(ws.partial, ws.seg_ptr, N, dkv);
     return hipGetLastError();
 }
@@ -224,7 +243,7 @@ hipError_t launch_gather_sum_phase(const uint16_t* interm, const int32_t* row_pt
     const int64_t ms = gather_max_segments(M, N);
     smla_k5_gather_segment<<<(unsigned)ms, kSegWaves * 64, 0, s>>>(interm, row_ptr, slots,
                                                                    ws.seg_ptr, ws.seg_row, N, M,
-                                                                   ws.partial);
+                                                                   ws.partial, nullptr);
     smla_k5_gather_combine_acc<<<(N + 3) / 4, 256, 0, s>>>(ws.partial, ws.seg_ptr, N, first ? 1 : 0,
                                                            run, dkv_last);
     return hipGetLastError();
