@@ -155,8 +155,9 @@ def cpu_baseline(w, n_tokens):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build has no "
-              "multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the library has no "
+              "multi-GPU path (how it would shard is described with the design); run with "
+              "--gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
