@@ -179,26 +179,20 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
 // multiple of 8, workgroup b runs on XCD b % 8 (blocks are dealt to the XCDs
 // in turn) and gets id (b % 8) * G/8 + b / 8 of every round: each XCD works on
 // neighbouring items (their tokens share kv rows in that XCD's L2), and every
-// XCD sees every part of the token range (balanced work).  Workgroups start
-// their round sequence at different points (eight per XCD and four groups
-// within an XCD), so they do not all switch items, and reload q/dO from HBM,
-// at the same moment.
+// XCD sees every part of the token range (balanced work).  All workgroups walk
+// the rounds in the same order, so the whole grid stays on one stretch of
+// tokens at a time (starting workgroups at staggered rounds, to spread their
+// item switches, was measured about 1% slower: it spreads the kv rows in use).
 struct ItemSeq {
-    int lo, step, n, r0;
+    int lo, step, n;
     __device__ ItemSeq(int b, int G, int n_items) {
         const bool xcd = (G & 7) == 0;
         lo = xcd ? (b & 7) * (G >> 3) + (b >> 3) : b;
         step = G;
         n = lo < n_items ? (n_items - lo + G - 1) / G : 0;
-        const int phase = xcd ? (b & 7) * 4 + ((b >> 3) * 4) / (G >> 3) : 0;  // 0..31
-        r0 = (int)((long long)phase * n / 32);
     }
     __device__ int count() const { return n; }
-    __device__ int item(int r) const {
-        int rr = r + r0;
-        if (rr >= n) rr -= n;
-        return lo + rr * step;
-    }
+    __device__ int item(int r) const { return lo + r * step; }
 };
 
 // Persistent producer/consumer variant for 64-head groups (H % 64 == 0): one
