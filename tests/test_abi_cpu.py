@@ -140,3 +140,14 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         B.lib()
+
+
+def test_traffic_hash_ignores_comments_only():
+    # the stored HBM-traffic figure is keyed to the kernel code without comments
+    import bench
+    a = "int f(int x) { // add one\n  return x + 1; /* done */ }\n"
+    b = "int f(int x) {\n\n  return x + 1;   }  // a different comment\n"
+    c = "int f(int x) { return x + 2; }"
+    assert bench._code_only(a) == bench._code_only(b)
+    assert bench._code_only(a) != bench._code_only(c)
+    assert len(bench.kernel_source_hash()) == 16
