@@ -594,13 +594,13 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         const int32_t* idx_next = has_next ? idx + (size_t)(seg_item(s + 1) / nhg) * K : idx;
         const int k0_next = has_next ? seg_k0(s + 1) : 0;
         if (!primed) {
-            // restart: copy tiles 0..2 of s, then produce tile 0
+            // restart: copy tiles 0 and 1 of s, then produce tile 0
             if constexpr (PROD) {
                 enter_segment(s, first_of_item);
             } else {
 #pragma unroll
-                for (int p = 0; p < kNBuf - 1; ++p) issue(&Lb[s & 1], p, base + p);
-                wait_vmcnt<2 * R>();
+                for (int p = 0; p < kNBuf - 2; ++p) issue(&Lb[s & 1], p, base + p);
+                wait_vmcnt<R>();
                 since = 0;
             }
             __syncthreads();
@@ -612,21 +612,16 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             const int pos = base + j;
             if constexpr (!PROD) {
                 // Tile pos+1 is produced in this iteration unless the stream ends.
-                // Vector memory ops complete in issue order, so the bound is the
-                // count of ops issued after its copies: tile pos+2's copies, the
-                // warming copies of the last two iterations (one each, none before
-                // a restart), and the dq stores of an epilogue run in one of the
-                // last two iterations.
+                // Its copies were issued in the previous iteration (two tiles ahead
+                // of the consumer, one ahead of the producer; a deeper lookahead
+                // was measured no faster).  Vector memory ops complete in issue
+                // order, so the bound is the count of ops issued after them: that
+                // iteration's warming copy (none right after a restart) and, if it
+                // ran an epilogue, its dq stores.
                 if (j + 1 < ntile || cont) {
-                    if (post_epi > 0) {
-                        if (since == 0) wait_vmcnt<R + kEpiStores>();
-                        else if (since == 1) wait_vmcnt<R + 1 + kEpiStores>();
-                        else wait_vmcnt<R + 2 + kEpiStores>();
-                    } else {
-                        if (since == 0) wait_vmcnt<R>();
-                        else if (since == 1) wait_vmcnt<R + 1>();
-                        else wait_vmcnt<R + 2>();
-                    }
+                    if (since == 0) wait_vmcnt<0>();
+                    else if (post_epi > 0) wait_vmcnt<1 + kEpiStores>();
+                    else wait_vmcnt<1>();
                 }
             }
             __syncthreads();
@@ -660,9 +655,9 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                     if (p_n > 0) produce(pos + 1, 0, NoReload{}, nullptr, nullptr);
                 }
             } else {
-                const int ahead = j + kNBuf - 1;
-                if (ahead < ntile || !cont) issue(&Lb[s & 1], ahead, pos + kNBuf - 1);
-                else issue(&Lb[(s + 1) & 1], ahead - ntile, pos + kNBuf - 1);
+                const int ahead = j + kNBuf - 2;
+                if (ahead < ntile || !cont) issue(&Lb[s & 1], ahead, pos + kNBuf - 2);
+                else issue(&Lb[(s + 1) & 1], ahead - ntile, pos + kNBuf - 2);
                 {
                     const int first = ntile > kWarmTiles + 2 ? ntile - kWarmTiles - 2 : 0;
                     const bool warm = next_new_item && j >= first && j + 2 < ntile;
@@ -673,7 +668,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 ++since;
                 if (j + 1 == ntile && last_of_item) {
                     epilogue(item, pos);
-                    post_epi = 2;
+                    post_epi = 1;   // the next iteration's wait skips these stores
                 }
             }
         }
