@@ -52,6 +52,18 @@ __device__ __forceinline__ void copy_row_to_lds(i32x4 rsrc, uint32_t lds, int vo
                  : "memory");
 }
 
+// The same copy with the non-temporal hint, for rows read exactly once.
+__device__ __forceinline__ void copy_row_to_lds_nt(i32x4 rsrc, uint32_t lds, int voffset) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                 :
+                 : "v"(voffset), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
+}
+
+// Cache-policy operand of the buffer store builtins: non-temporal (gfx950 "nt" bit).
+constexpr int kCacheNT = 2;
+
 // Buffer resource over [p, p + bytes): loads outside the range return zeros.
 __device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(p);
