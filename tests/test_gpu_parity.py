@@ -293,9 +293,15 @@ def test_forward_matches_oracle(name, sink):
     (23, 128, 60, 33, False),   # two 64-head groups, 2 tiles per token, no sink
     (50, 64, 50, 1, True),      # topk = 1: every token has at most one tile
     (9, 64, 300, 96, True),     # most kv rows unused
+    (19, 32, 19, 16, True),     # one-wave-per-16-heads kernel, two waves per block
+    (21, 96, 45, 64, False),    # the same kernel with three head blocks, no sink
+    (25, 48, 33, 40, True),     # one wave per block
+    (12, 64, 80, 600, True),    # topk beyond one index chunk: four waves per block
 ])
 def test_forward_ragged(T, H, N, K, sink):
     x = _custom(T, H, N, K, seed=7 * T + H, sink=sink, pool_frac=0.5)
+    if K > 512:
+        x["idx"] = inputs.shuffle_slots(x["idx"], seed=T + K)   # valid slots in both chunks
     x["idx"][2] = -1                                    # an all-masked token
     _say(f"[fwd ragged] T={T} H={H} N={N} K={K} sink={sink}")
     O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
@@ -384,6 +390,7 @@ def _oracle_inputs(x):
     (33, 80, 40, 70, False, False),   # 1-wave head groups, no sink
     (17, 112, 30, 33, True, False),
     (9, 128, 300, 96, True, False),   # most kv rows unused
+    (21, 96, 45, 64, True, False),    # 6 reduction steps in the intermediate, 2-wave dQ blocks
     (37, 48, 53, 40, True, True),     # with dlse: the all-masked row gets P_sink = 1
     (33, 80, 40, 70, False, True),    # with dlse, no sink: the all-masked row stays zero
 ])
