@@ -10,8 +10,9 @@ workspace and outputs are preallocated, so nothing is allocated while timing.
 
 Prints ONE JSON line: value = nominal TFLOPS (10*T*H*topk*512 flops per call,
 padded slots counted), ms_per_step, the roofline of the dominant kernel
-(timed live with HIP events on the library's stream) and, on rank 0 at N=1,
-the fp64 CPU oracle timed on a bounded sample of the same workload.
+(timed live inside the timed calls with HIP events that the library records on
+the calls' stream at its stage boundaries) and, on rank 0 at N=1, the fp64 CPU
+oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=3072,
                     help="tokens of the oracle baseline sample (about 10 s of host work)")
     ap.add_argument("--stage-steps", type=int, default=10)
+    ap.add_argument("--stage-events", choices=["on", "off"], default="on",
+                    help="time delta/dQ/intermediate/gather with events recorded inside the "
+                         "timed calls (off: plain calls, stages timed through their entry points)")
     ap.add_argument("--mode", choices=["full", "profile"], default="full",
                     help="profile: only the timed backward calls, then a plain device copy of "
                          "COPY_BYTES (the reference for scaling HBM byte counters); prints no JSON")
@@ -191,21 +195,28 @@ def main():
     ws = B.bwd_workspace(T, H, N, K, q.device)
     torch.cuda.synchronize()
 
-    def step():
-        B.smla_bwd(q, kv, dO, O, lse, idx, sink, scale, workspace=ws, out=(dq, dkv, d_sink))
+    def step(events=None):
+        B.smla_bwd(q, kv, dO, O, lse, idx, sink, scale, workspace=ws, out=(dq, dkv, d_sink),
+                   events=events)
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    # ---- timed region: exactly K steps between synchronisations
+    # ---- timed region: exactly K steps between synchronisations.  Each call also
+    # records five events on its stream at its stage boundaries (smla_bwd_timed),
+    # which time delta, dQ, the intermediate and the gather inside the real calls.
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for evs in sev:
+        for e in evs:
+            e.record()      # creates the event
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev[0].record()
     for i in range(args.steps):
-        step()
+        step(sev[i] if args.stage_events == "on" else None)
         ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -225,7 +236,10 @@ def main():
               f"{COPY_BYTES} bytes", file=sys.stderr, flush=True)
         return
 
-    # ---- per-stage timing (each stage entry point alone, same stream, same buffers)
+    # ---- per-stage timing: delta, dQ, the intermediate and the gather from the
+    # events inside the timed calls; the CSR build and d_sink, which run hidden on
+    # the library's helper stream there, from their entry points called alone
+    # (same stream, same buffers)
     delta = torch.empty((T, H), dtype=torch.float32, device="cuda")
     dsp = torch.empty((B.dsp_numel(T, H, K),), dtype=torch.bfloat16, device="cuda")
     interm = torch.empty((T * K, D), dtype=torch.bfloat16, device="cuda")
@@ -246,6 +260,11 @@ def main():
         "dsink": lambda: B.smla_dsink(lse, delta, sink, d_sink=ds2, workspace=s_ws),
     }
     stage_ms = {}
+    in_step = ("delta", "dq", "interm", "gather")
+    if args.stage_events == "on":
+        for k, name in enumerate(in_step):
+            stage_ms[name] = float(np.mean([e[k].elapsed_time(e[k + 1]) for e in sev]))
+        stages = {k: v for k, v in stages.items() if k not in in_step}
     for name, fn in stages.items():
         fn()
         torch.cuda.synchronize()
@@ -343,6 +362,8 @@ def main():
                    "global_batch": T, "seq_len": T, "parallelism": "none (1 GPU)",
                    "valid_slots": nnz},
         "stages": stage_rows,
+        "stages_timed": ("delta, dq, interm, gather: events inside the timed calls; csr, dsink: "
+                         "entry points alone" if args.stage_events == "on" else "entry points alone"),
         "forward": forward,
         "phased": phased_row,
         "roofline": roofline,

@@ -120,6 +120,24 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
              uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * smla_bwd_timed -- smla_bwd (same arguments, same kernels, same results) that
+ * also records five caller-owned events on `stream`, so that a caller can time
+ * each stage inside a real call: events[0] before delta, [1] after delta,
+ * [2] after dQ, [3] after the intermediate, [4] after the gather (including its
+ * wait for the helper stream's CSR build).  Page: aiter PR 4766, Structure table
+ * (the per-phase split the events follow).
+ *   events  array of 5 hipEvent_t created by the caller on the current device
+ *           (timing enabled); the library only records them.
+ * Errors: as smla_bwd; a NULL array or NULL event is SMLA_ERR_INVALID_ARG
+ * (before any launch); a failed record is SMLA_ERR_HIP.
+ */
+int smla_bwd_timed(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+                   const float* lse, const int32_t* idx, const float* sink, const float* dlse,
+                   int T, int H, int num_kv, int topk, float scale,
+                   uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
+                   void* workspace, size_t workspace_bytes, void* stream, void* const* events);
+
 /* Bytes of workspace smla_bwd_phased needs (0 on a shape error or phase_tokens < 1). */
 size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int phase_tokens);
 

@@ -34,6 +34,8 @@ _SIGNATURES = {
     "smla_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "smla_bwd_workspace_bytes": ([_I, _I, _I, _I], _Z),
     "smla_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "smla_bwd_timed": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P,
+                        _P], _I),
     "smla_bwd_phased_workspace_bytes": ([_I, _I, _I, _I, _I], _Z),
     "smla_bwd_phased": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _Z,
                          _P], _I),
@@ -157,11 +159,14 @@ def bwd_workspace(T, H, num_kv, topk, device):
 
 
 def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=None,
-             count_invalid=False, dlse=None):
+             count_invalid=False, dlse=None, events=None):
     """Sparse MLA backward: returns (dq, dkv, d_sink[, n_invalid]).
 
     out, if given, is a tuple (dq, dkv, d_sink) of preallocated outputs.
     dlse, if given, is the upstream gradient of lse (fp32 [T, H]).
+    events, if given, are five torch.cuda.Event objects (timing enabled) that the
+    call records on its stream at the stage boundaries (smla_bwd_timed): before
+    delta and after delta, dQ, the intermediate and the gather.
     """
     T, H, _ = q.shape
     N, K = kv.shape[0], idx.shape[1]
@@ -184,10 +189,19 @@ def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=
     if workspace is None:
         workspace = bwd_workspace(T, H, N, K, q.device)
     n_inv = torch.empty((1,), dtype=torch.int32, device=q.device) if count_invalid else None
-    _check("smla_bwd", lib().smla_bwd(
-        _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
-        _default_scale(scale), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
-        _ptr(workspace), workspace.numel(), _stream(q.device)))
+    args = (_ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
+            _default_scale(scale), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
+            _ptr(workspace), workspace.numel(), _stream(q.device))
+    if events is None:
+        _check("smla_bwd", lib().smla_bwd(*args))
+    else:
+        if len(events) != 5:
+            raise ValueError("smla_bwd: events must hold five torch.cuda.Event objects")
+        for e in events:
+            if e.cuda_event == 0:   # torch creates the underlying event at its first record
+                e.record()
+        handles = (ctypes.c_void_p * 5)(*[e.cuda_event for e in events])
+        _check("smla_bwd_timed", lib().smla_bwd_timed(*args, handles))
     if count_invalid:
         return dq, dkv, d_sink, n_inv
     return dq, dkv, d_sink

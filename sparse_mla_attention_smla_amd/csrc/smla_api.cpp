@@ -253,10 +253,16 @@ int smla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const fl
                                  static_cast<hipStream_t>(stream)));
 }
 
-int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+}  // extern "C"
+
+namespace {
+// The whole backward; when `ev` is given, its five events are recorded on the
+// caller's stream before delta and after delta, dQ, the intermediate and the gather.
+int bwd_impl(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
              const float* lse, const int32_t* idx, const float* sink, const float* dlse, int T,
              int H, int num_kv, int topk, float scale, uint16_t* dq, uint16_t* dkv, float* d_sink,
-             int32_t* n_invalid, void* workspace, size_t workspace_bytes, void* stream) {
+             int32_t* n_invalid, void* workspace, size_t workspace_bytes, void* stream,
+             void* const* ev) {
     smla_status st = check_shape(T, H, num_kv, topk);
     if (st != SMLA_OK) return st;
     if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
@@ -316,7 +322,12 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
     }
     if (launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, aux) != hipSuccess) return SMLA_ERR_HIP;
     if (launch_gather_plan(row_ptr, M, num_kv, gs, aux) != hipSuccess) return SMLA_ERR_HIP;
+    auto mark = [&](int i) {
+        return ev == nullptr || hipEventRecord(static_cast<hipEvent_t>(ev[i]), s) == hipSuccess;
+    };
+    if (!mark(0)) return SMLA_ERR_HIP;
     if (launch_delta(o, dO, dlse, (int64_t)T * H, delta, s) != hipSuccess) return SMLA_ERR_HIP;
+    if (!mark(1)) return SMLA_ERR_HIP;
     if (sink != nullptr) {
         if (side != nullptr && (hipEventRecord(side->after_delta, s) != hipSuccess ||
                                 hipStreamWaitEvent(aux, side->after_delta, 0) != hipSuccess))
@@ -327,12 +338,38 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
     if (side != nullptr && hipEventRecord(side->join, aux) != hipSuccess) return SMLA_ERR_HIP;
     if (launch_dq(q, kv, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dsp, s) != hipSuccess)
         return SMLA_ERR_HIP;
+    if (!mark(2)) return SMLA_ERR_HIP;
     if (launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm, s) != hipSuccess)
         return SMLA_ERR_HIP;
+    if (!mark(3)) return SMLA_ERR_HIP;
     if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SMLA_ERR_HIP;
     if (launch_gather_sum(interm, row_ptr, slots, M, num_kv, gs, dkv, s) != hipSuccess)
         return SMLA_ERR_HIP;
+    if (!mark(4)) return SMLA_ERR_HIP;
     return SMLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+             const float* lse, const int32_t* idx, const float* sink, const float* dlse, int T,
+             int H, int num_kv, int topk, float scale, uint16_t* dq, uint16_t* dkv, float* d_sink,
+             int32_t* n_invalid, void* workspace, size_t workspace_bytes, void* stream) {
+    return bwd_impl(q, kv, dO, o, lse, idx, sink, dlse, T, H, num_kv, topk, scale, dq, dkv, d_sink,
+                    n_invalid, workspace, workspace_bytes, stream, nullptr);
+}
+
+int smla_bwd_timed(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+                   const float* lse, const int32_t* idx, const float* sink, const float* dlse,
+                   int T, int H, int num_kv, int topk, float scale, uint16_t* dq, uint16_t* dkv,
+                   float* d_sink, int32_t* n_invalid, void* workspace, size_t workspace_bytes,
+                   void* stream, void* const* events) {
+    if (events == nullptr) return SMLA_ERR_INVALID_ARG;
+    for (int i = 0; i < 5; ++i)
+        if (events[i] == nullptr) return SMLA_ERR_INVALID_ARG;
+    return bwd_impl(q, kv, dO, o, lse, idx, sink, dlse, T, H, num_kv, topk, scale, dq, dkv, d_sink,
+                    n_invalid, workspace, workspace_bytes, stream, events);
 }
 
 int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,

@@ -34,7 +34,7 @@ def lib():
 
 def test_header_and_binding_agree(lib):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     assert sorted(B.EXPORTED) == names
 
 
@@ -103,6 +103,19 @@ def test_bwd_argument_errors(lib):
     assert _bwd(lib, dlse=12 * A) in (HIP, ARCH)          # dlse is optional
     # a valid call gets past validation and then needs a gfx950 device
     assert _bwd(lib) in (HIP, ARCH)
+
+
+def test_timed_bwd_argument_errors(lib):
+    import ctypes
+    p = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, None, 64, 16, 64, 16, 0.05,
+         8 * A, 9 * A, 10 * A, None, 11 * A, 1 << 34, None]
+    assert lib.smla_bwd_timed(*p, None) == INVALID                       # no event array
+    evs = (ctypes.c_void_p * 5)(1, 2, None, 4, 5)
+    assert lib.smla_bwd_timed(*p, evs) == INVALID                        # a NULL event
+    full = (ctypes.c_void_p * 5)(1, 2, 3, 4, 5)
+    bad = list(p)
+    bad[10] = 63                                                         # num_kv < T
+    assert lib.smla_bwd_timed(*bad, full) == SHAPE
 
 
 def test_phased_argument_errors(lib):

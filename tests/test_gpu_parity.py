@@ -200,6 +200,22 @@ def test_deterministic_and_poisoned_workspace(small_case):
         assert torch.equal(a[2], b[2]) and torch.equal(a[2], c[2])
 
 
+def test_timed_call_equals_plain_call(small_case):
+    """smla_bwd_timed does the same work as smla_bwd (bit for bit) and records its
+    five stage events in order on the call's stream."""
+    name, x, ref, d = small_case
+    a = _run_bwd(d)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    b = _run_bwd(d, events=evs)
+    for i in range(2):
+        assert torch.equal(host_bits_t(a[i]), host_bits_t(b[i]))
+    if a[2] is not None:
+        assert torch.equal(a[2], b[2])
+    spans = [evs[k].elapsed_time(evs[k + 1]) for k in range(4)]
+    assert all(t >= 0.0 for t in spans), spans
+    assert spans[1] > 0.0                                   # dQ ran between events 1 and 2
+
+
 def test_concurrent_calls_from_two_threads(small_case):
     """Two host threads, each on its own stream, call smla_bwd at the same time
     (the enqueues share the library's helper stream); both results must equal
