@@ -429,6 +429,65 @@ def test_ragged_shapes(T, H, N, K, sink, with_dlse):
         assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
 
 
+def _fuzz_case(seed):
+    """A random small problem: any H the library takes, topk up to two index chunks,
+    slots drawn with replacement (duplicate rows within a token), -1 padding and a
+    few out-of-range values mixed in anywhere."""
+    rng = np.random.default_rng([77, seed])
+    T = int(rng.integers(1, 41))
+    H = int(rng.choice([16, 32, 48, 64, 80, 96, 112, 128]))
+    N = T + int(rng.integers(0, 120))
+    K = int(rng.choice([1, 7, 16, 31, 32, 33, 64, 100, 512, 513, 600]))
+    idx = rng.integers(0, N, size=(T, K)).astype(np.int32)
+    idx = np.where(rng.random((T, K)) < 0.25, -1, idx)
+    bad = rng.random((T, K)) < 0.02
+    idx = np.where(bad, np.where(rng.random((T, K)) < 0.5, -5, N + 2), idx).astype(np.int32)
+    sink = bool(rng.integers(0, 2))
+    x = {"q": inputs.normal_bf16((T, H, 512), 5000 + seed, 1), "kv": inputs.normal_bf16((N, 512), 5000 + seed, 2),
+         "dO": inputs.normal_bf16((T, H, 512), 5000 + seed, 3), "idx": idx,
+         "sink": rng.standard_normal(H).astype(np.float32) if sink else None}
+    dlse = rng.standard_normal((T, H)).astype(np.float32) if rng.integers(0, 2) else None
+    return x, dlse
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_problems(seed):
+    x, dlse = _fuzz_case(seed)
+    T, H, _ = x["q"].shape
+    N, K = x["kv"].shape[0], x["idx"].shape[1]
+    dups = sum(int(np.unique(r[r >= 0]).size < (r >= 0).sum()) for r in x["idx"])
+    _say(f"[fuzz {seed}] T={T} H={H} N={N} K={K} sink={x['sink'] is not None} "
+         f"dlse={dlse is not None} rows with duplicates={dups}")
+    x = _oracle_inputs(x)
+    d = _to_dev(x)
+    # forward
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    o, lse = B.smla_fwd(d["q"], d["kv"], d["idx"], d["sink"], SCALE)
+    torch.cuda.synchronize()
+    assert_close("O", host_bf16(o), O64)
+    got = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(lse64)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert np.max(np.abs(got[fin] - lse64[fin]), initial=0.0) < 1e-4
+    # backward
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE, dlse=dlse)
+    dq, dkv, ds, n_inv = _run_bwd(d, dlse=None if dlse is None else dev(dlse), count_invalid=True)
+    assert int(n_inv.item()) == orc.count_invalid(x["idx"], N)
+    for name, g, r in (("dq", host_bf16(dq), ref["dq"]), ("dkv", host_bf16(dkv), ref["dkv"])):
+        if np.linalg.norm(r) == 0.0:
+            assert np.all(g == 0.0), name
+        else:
+            assert_close(name, g, r)
+    if x["sink"] is not None:
+        assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
+    unused = np.setdiff1d(np.arange(N), x["idx"][(x["idx"] >= 0) & (x["idx"] < N)])
+    assert np.all(host_bf16(dkv)[unused] == 0.0)
+    row_ptr, slots = B.smla_build_csr(d["idx"], N)
+    rp, sl = orc.csr(x["idx"], N)
+    assert np.array_equal(row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(slots.cpu().numpy()[: rp[-1]], sl)
+
+
 @pytest.mark.parametrize("H,sink", [(64, True), (128, False)])
 def test_topk_beyond_one_chunk(H, sink):
     """topk > 512: each token's slots form several 512-slot segments (the last
