@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=3072,
                     help="tokens of the oracle baseline sample (about 10 s of host work)")
     ap.add_argument("--stage-steps", type=int, default=10)
+    ap.add_argument("--graph", choices=["on", "off"], default="on",
+                    help="also time the call captured in a HIP graph and replayed")
     ap.add_argument("--stage-events", choices=["on", "off"], default="on",
                     help="time delta/dQ/intermediate/gather with events recorded inside the "
                          "timed calls (off: plain calls, stages timed through their entry points)")
@@ -93,6 +95,33 @@ def stored_traffic(kernel: str):
         return None
     k = rec.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
+
+
+def time_graph(w, step, reps):
+    """ms per call when one smla_bwd call, captured in a HIP graph on a side stream,
+    is replayed (same kernels, same buffers; the graph holds no allocation)."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(s)
+        for _ in range(reps):
+            g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    return {"ms": round(ms, 4), "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 1),
+            "note": "the same call captured once in a HIP graph and replayed (launch gaps only differ)"}
 
 
 def time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq, dkv, ds, reps):
@@ -330,6 +359,7 @@ def main():
     # the bounded-workspace backward (token phases of 1024) on the same inputs
     phased_row = None
     ph_tokens = 1024
+    graph_row = time_graph(w, step, args.steps) if args.graph == "on" else None
     if args.phased == "on":
         phased_row = time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq2, dkv2,
                                  ds2, args.stage_steps)
@@ -366,6 +396,7 @@ def main():
                          "entry points alone" if args.stage_events == "on" else "entry points alone"),
         "forward": forward,
         "phased": phased_row,
+        "graph_replay": graph_row,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "context": {"pages_own_backward_mi355x": {"ms": 3.238, "tflops": 424},
