@@ -47,8 +47,9 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=3072,
                     help="tokens of the oracle baseline sample (about 10 s of host work)")
     ap.add_argument("--stage-steps", type=int, default=10)
-    ap.add_argument("--graph", choices=["on", "off"], default="on",
-                    help="also time the call captured in a HIP graph and replayed")
+    ap.add_argument("--graph", choices=["on", "off"], default="off",
+                    help="also time the call captured in a HIP graph and replayed (off by default "
+                         "so that the default run's kernel trace holds only the measured calls)")
     ap.add_argument("--stage-events", choices=["on", "off"], default="on",
                     help="time delta/dQ/intermediate/gather with events recorded inside the "
                          "timed calls (off: plain calls, stages timed through their entry points)")
