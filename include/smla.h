@@ -16,7 +16,7 @@
  *    accumulated into).
  *  - D (head dimension) is fixed at 512.  Shapes: T query tokens, H heads,
  *    num_kv kv rows, topk index slots per token.  Limits (else SMLA_ERR_SHAPE):
- *    T >= 0, 16 <= H <= 128 with H % 16 == 0, topk >= 1, T*topk < 2^31,
+ *    T >= 0, 16 <= H <= 128 with H % 16 == 0, 1 <= topk <= 2^20, T*topk < 2^31,
  *    num_kv >= max(T, 1) (the Contract section allows num_kv > T: rows past T
  *    are a compressed pool) and num_kv < 2^20.
  *  - Index values outside [0, num_kv) are masked like -1 (never read); values

@@ -21,6 +21,7 @@ using namespace smla;
 namespace {
 
 constexpr int kMaxDevices = 64;
+constexpr int kMaxTopk = 1 << 20;  // index slots per token
 int g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::mutex g_arch_mu;
 
@@ -114,6 +115,9 @@ smla_status check_shape(int T, int H, int num_kv, int topk) {
     if (T < 0 || H < 16 || H > 128 || H % 16 != 0 || topk < 1) return SMLA_ERR_SHAPE;
     if (num_kv < 1 || num_kv < T || num_kv >= (1 << 20)) return SMLA_ERR_SHAPE;
     if ((int64_t)T * topk >= (int64_t)1 << 31) return SMLA_ERR_SHAPE;
+    // a token's intermediate block (topk rows of 1 KiB) is addressed with
+    // 32-bit buffer offsets
+    if (topk > kMaxTopk) return SMLA_ERR_SHAPE;
     return SMLA_OK;
 }
 

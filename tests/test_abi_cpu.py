@@ -85,6 +85,8 @@ def test_bwd_argument_errors(lib):
     assert _bwd(lib, H=24) == SHAPE
     assert _bwd(lib, H=144) == SHAPE
     assert _bwd(lib, K=0) == SHAPE
+    assert _bwd(lib, T=1, N=64, K=(1 << 20) + 16) == SHAPE    # topk past the 32-bit row offsets
+    assert lib.smla_bwd_workspace_bytes(1, 16, 64, (1 << 20) + 16) == 0
     assert _bwd(lib, N=63) == SHAPE                       # num_kv < T
     assert _bwd(lib, N=1 << 20) == SHAPE
     assert _bwd(lib, T=1 << 20, N=1 << 20 - 1, K=4096) == SHAPE
