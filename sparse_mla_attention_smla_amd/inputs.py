@@ -74,6 +74,9 @@ WORKLOADS = {
                        selection="swa_pool_zipf", window=128, pool_stride=4, pool_picks=384),
     "long": Workload("long", 4, T=8192, H=128, num_kv=10240, topk=512,
                      selection="swa_pool", window=128, pool_stride=4, pool_picks=384),
+    # the page's correctness runs also use H = 64
+    "headline_h64": Workload("headline_h64", 5, T=4096, H=64, num_kv=5120, topk=512,
+                             selection="swa_pool", window=128, pool_stride=4, pool_picks=384),
 }
 
 

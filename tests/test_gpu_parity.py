@@ -692,7 +692,7 @@ def test_phased_headline_sampled():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,with_dlse", [("headline", False), ("skewed", False), ("long", False),
-                                            ("headline", True)])
+                                            ("headline", True), ("headline_h64", False)])
 def test_full_size_sampled(name, with_dlse):
     _say(f"[full] {name}: generating inputs and the oracle forward (dlse={with_dlse})")
     x = workload(name)

@@ -466,7 +466,8 @@ def test_page_flop_convention_and_interm_size():
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,nnz", [("tiny", 904), ("small", 122_944), ("headline", 1_793_728),
-                                      ("skewed", 1_793_728), ("long", 3_890_880)])
+                                      ("skewed", 1_793_728), ("long", 3_890_880),
+                                      ("headline_h64", 1_793_728)])
 def test_generator_index_structure(name, nnz):
     w = inputs.WORKLOADS[name]
     idx = inputs.make_indices(w, np.random.default_rng(1000 + w.index))
