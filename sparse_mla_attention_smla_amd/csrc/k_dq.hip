@@ -33,7 +33,7 @@ template <int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
 void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 const uint16_t* __restrict__ dO, const float* __restrict__ lse,
-                const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
+                const float* __restrict__ delta, const int32_t* __restrict__ idx, int H,
                 int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
     static_assert(kNBuf == 4, "the vmcnt bounds below assume a 4-deep ring");
     constexpr int R = kBK / NW;   // DMA copies per wave per tile
@@ -773,8 +773,8 @@ hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, 
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
-    if (nw == 2) smla_k2_dq<2><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
-    else smla_k2_dq<1><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
+    if (nw == 2) smla_k2_dq<2><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp);
+    else smla_k2_dq<1><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp);
     return hipGetLastError();
 }
 

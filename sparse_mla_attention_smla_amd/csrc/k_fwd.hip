@@ -20,7 +20,7 @@ namespace smla {
 template <int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
 void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-                 const int32_t* __restrict__ idx, const float* __restrict__ sink, int T, int H,
+                 const int32_t* __restrict__ idx, const float* __restrict__ sink, int H,
                  int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse) {
     constexpr int R = kBK / NW;
     __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
@@ -152,9 +152,9 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
     const int nw = dq_waves(H);
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
     switch (nw) {
-        case 4: smla_k7_fwd<4><<<blocks, 256, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse); break;
-        case 2: smla_k7_fwd<2><<<blocks, 128, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse); break;
-        default: smla_k7_fwd<1><<<blocks, 64, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse); break;
+        case 4: smla_k7_fwd<4><<<blocks, 256, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse); break;
+        case 2: smla_k7_fwd<2><<<blocks, 128, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse); break;
+        default: smla_k7_fwd<1><<<blocks, 64, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse); break;
     }
     return hipGetLastError();
 }

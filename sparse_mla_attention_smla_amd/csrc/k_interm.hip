@@ -40,7 +40,7 @@ constexpr int kOBytes = kBK * kOPitch;                  // one tile of output ro
 template <int NKS>
 __global__ __attribute__((amdgpu_flat_work_group_size(kIThreads, kIThreads), amdgpu_waves_per_eu(2, 2)))
 void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dO,
-                    const uint16_t* __restrict__ dsp, const int32_t* __restrict__ idx, int T,
+                    const uint16_t* __restrict__ dsp, const int32_t* __restrict__ idx,
                     int N, int K, uint16_t* __restrict__ interm) {
     constexpr int H = NKS * 16;
     constexpr int R = 2 * H;
@@ -213,7 +213,7 @@ hipError_t launch_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* 
                          hipStream_t s) {
     if (T == 0) return hipSuccess;
 #define SMLA_INTERM_CASE(nks) \
-    case nks: smla_k3_interm<nks><<<T, kIThreads, 0, s>>>(q, dO, dsp, idx, T, N, K, interm); break;
+    case nks: smla_k3_interm<nks><<<T, kIThreads, 0, s>>>(q, dO, dsp, idx, N, K, interm); break;
     switch (H / 16) {
         SMLA_INTERM_CASE(1)
         SMLA_INTERM_CASE(2)
