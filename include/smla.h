@@ -182,11 +182,14 @@ int smla_delta(const uint16_t* o, const uint16_t* dO, const float* dlse, int T, 
  *   dq  bf16 [T, H, 512] out
  *   dsp bf16 out, smla_dsp_bytes() bytes: per token t, the valid slots of its
  *       index row (in increasing slot order, taken in runs of 512 slots) are
- *       grouped in tiles of 32; tile c of token t is the block
- *       dsp[((t*ceil(topk/32) + c) * 2H + r) * 32 + j], r < 2H, j < 32, with
- *       row r = h holding scale*dS[t,h,slot_j] and row r = H + h holding
- *       P[t,h,slot_j]; columns past the last valid slot of a run hold 0, and
- *       blocks past the token's last tile are left unwritten.
+ *       grouped in tiles of 32; tile c of token t is the block of 2H*32 values
+ *       at dsp + (t*ceil(topk/32) + c) * 2H*32, holding for rows r < 2H (r = h:
+ *       scale*dS[t,h,.], r = H + h: P[t,h,.]) and tile slots j < 32 the value
+ *       of (r, j) at block offset (r/16)*512 + ((j%16)/4*16 + r%16)*8 + (j/16)*4
+ *       + j%4 (the "piece layout": 16-row chunks of 64 pieces of 8 values, piece
+ *       g*16 + r%16 holding slots 4g..4g+3 and 16+4g..16+4g+3 of row r, the order
+ *       in which the MFMA lanes hold them); slots past the last valid slot of a
+ *       run hold 0, and blocks past the token's last tile are left unwritten.
  */
 int smla_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const float* lse,
             const float* delta, const int32_t* idx, int T, int H, int num_kv, int topk,

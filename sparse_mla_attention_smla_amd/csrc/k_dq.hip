@@ -116,16 +116,16 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                         ps[st][i] = p;
                         dss[st][i] = p * (pacc[st][i] - dl) * scale;
                     }
-                uint16_t* blk = dsp_tok + (size_t)(ctg + j) * (2 * H) * kBK;
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    *reinterpret_cast<u32x2*>(blk + (size_t)h * kBK + 16 * st + 4 * g) =
-                        u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])};
-                    *reinterpret_cast<u32x2*>(blk + (size_t)(H + h) * kBK + 16 * st + 4 * g) =
-                        u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])};
-                }
-                return u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
-                             pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
+                // one 16-byte piece per lane and kind (dsp piece layout): the
+                // lanes of a wave write 1 KiB contiguously
+                uint16_t* blk = dsp_tok + (size_t)(ctg + j) * (2 * H) * kBK + (size_t)(h - c16) * kBK + lane * 8;
+                const u32x4 dsv = {pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
+                                   pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
+                *reinterpret_cast<u32x4*>(blk) = dsv;
+                *reinterpret_cast<u32x4*>(blk + (size_t)H * kBK) =
+                    u32x4{pack_bf16(ps[0][0], ps[0][1]), pack_bf16(ps[0][2], ps[0][3]),
+                          pack_bf16(ps[1][0], ps[1][1]), pack_bf16(ps[1][2], ps[1][3])};
+                return dsv;
             };
             for (int j = 0; j + 1 < ntile; ++j) {
                 // Only the copies of tile j+2 are younger loads than those of tile
@@ -467,20 +467,18 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                     ps[st][i] = p;
                     dss[st][i] = p * (pacc[st][i] - dl) * scale;
                 }
-            // dsp rows of this wave's 16 heads, quad-contiguous: lane 4*c + g stores
-            // head (p_h - c16 + c), columns 16st + 4g .. +3
-            uint16_t* blk = p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK +
-                            (size_t)(p_h - c16 + (lane >> 2)) * kBK + 4 * (lane & 3);
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                *reinterpret_cast<u32x2*>(blk + 16 * st) = to_quad_rows(
-                    u32x2{pack_bf16(dss[st][0], dss[st][1]), pack_bf16(dss[st][2], dss[st][3])}, lane);
-                *reinterpret_cast<u32x2*>(blk + (size_t)H * kBK + 16 * st) = to_quad_rows(
-                    u32x2{pack_bf16(ps[st][0], ps[st][1]), pack_bf16(ps[st][2], ps[st][3])}, lane);
-            }
-            sh.dsfrag[pos & 1][w][lane] =
-                u32x4{pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
-                      pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
+            // dsp pieces of this wave's 16 heads: lane l = c16 + 16g holds the 8
+            // slots 4g..4g+3 and 16+4g..16+4g+3 of head c16, which is piece l of
+            // the heads' 1 KiB chunk (dsp piece layout), so each store writes
+            // 1 KiB contiguously from the MFMA lanes as they are (no permutation)
+            uint16_t* blk = p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK + (size_t)(p_h - c16) * kBK + lane * 8;
+            const u32x4 dsv = {pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
+                               pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
+            *reinterpret_cast<u32x4*>(blk) = dsv;
+            *reinterpret_cast<u32x4*>(blk + (size_t)H * kBK) =
+                u32x4{pack_bf16(ps[0][0], ps[0][1]), pack_bf16(ps[0][2], ps[0][3]),
+                      pack_bf16(ps[1][0], ps[1][1]), pack_bf16(ps[1][2], ps[1][3])};
+            sh.dsfrag[pos & 1][w][lane] = dsv;
         }
     };
     using NoReload = std::integral_constant<bool, false>;

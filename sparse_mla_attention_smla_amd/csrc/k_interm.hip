@@ -128,12 +128,15 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             if (id < kYChunks) pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + id * 8));
         }
     };
+    // piece id of the block (dsp piece layout): chunk id/64 of 16 rows, row
+    // 16*(id/64) + id%16, positions 8g..8g+7 with g = (id/16)%4
     auto store_tile = [&](char* yb_lds) {
 #pragma unroll
         for (int i = 0; i < kYPT; ++i) {
             const int id = tid + kIThreads * i;
             if (id < kYChunks)
-                *reinterpret_cast<u32x4*>(yb_lds + (id >> 2) * kYPitch + (id & 3) * 16) = pre[i];
+                *reinterpret_cast<u32x4*>(yb_lds + ((id >> 6) * 16 + (id & 15)) * kYPitch +
+                                          ((id >> 4) & 3) * 16) = pre[i];
         }
     };
 
@@ -194,11 +197,12 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             }
             __syncthreads();
             // whole 1 KiB rows leave with one non-temporal store each (wave w
-            // writes tile rows w, w+8, w+16, w+24)
+            // writes tile rows w, w+8, w+16, w+24); row r is position r of the
+            // block, i.e. slot 4(r/8) + r%4 (+16 when r%8 >= 4) of the tile
 #pragma unroll
             for (int i = 0; i < kBK / kIWaves; ++i) {
                 const int r = w + kIWaves * i;
-                const int pos = it * kBK + r;
+                const int pos = it * kBK + ((r & 4) << 2) + ((r >> 3) << 2) + (r & 3);
                 const u32x4 v = *reinterpret_cast<const u32x4*>(obuf + r * kOPitch + lane * 16);
                 const int voff = pos < n ? L.slot[pos] * (kD * 2) + lane * 16 : K * kD * 2;
                 __builtin_amdgcn_raw_buffer_store_b128(v, out_rsrc, voff, 0, kCacheNT);

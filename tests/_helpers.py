@@ -86,6 +86,19 @@ def host_bits(t) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
+def dsp_to_logical(vals, H):
+    """dS/P blocks in the library's piece layout (include/smla.h, smla_dq) ->
+    [..., 2H, 32] arrays indexed (row, tile slot).  Pure index bookkeeping."""
+    v = np.asarray(vals).reshape(-1, 2 * H // 16, 4, 16, 2, 4)   # chunk, g, row%16, half, i
+    return v.transpose(0, 1, 3, 4, 2, 5).reshape(-1, 2 * H, 32)  # chunk, row%16, half, g, i
+
+
+def dsp_from_logical(blocks, H):
+    """Inverse of dsp_to_logical: [..., 2H, 32] -> flat piece-layout values."""
+    v = np.asarray(blocks).reshape(-1, 2 * H // 16, 16, 2, 4, 4)  # chunk, row%16, half, g, i
+    return v.transpose(0, 1, 4, 2, 3, 5).reshape(-1)
+
+
 def dsp_map(idx, num_kv, chunk=512, bk=32):
     """Where each valid slot lives in the dS/P block buffer of smla_dq (the layout
     documented in include/smla.h): per token, valid slots in increasing order,

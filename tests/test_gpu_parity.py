@@ -15,8 +15,9 @@ import pytest
 
 from oracle import smla_oracle as orc
 from sparse_mla_attention_smla_amd import inputs
-from tests._helpers import (SCALE, assert_close, dev, dev_bf16, dsp_map, host_bf16, host_bits,
-                            rel_l2, workload, workload_nosink)
+from tests._helpers import (SCALE, assert_close, dev, dev_bf16, dsp_from_logical, dsp_map,
+                            dsp_to_logical, host_bf16, host_bits, rel_l2, workload,
+                            workload_nosink)
 
 pytestmark = pytest.mark.gpu
 
@@ -106,7 +107,7 @@ def test_stage_dq_and_dsp(small_case):
     T, K = x["idx"].shape
     H = x["q"].shape[1]
     ntk = (K + 31) // 32
-    got = host_bf16(dsp).reshape(T, ntk, 2 * H, 32)
+    got = dsp_to_logical(host_bf16(dsp), H).reshape(T, ntk, 2 * H, 32)
     t, b, c, k = dsp_map(x["idx"], x["kv"].shape[0])
     got_ds = got[t, b, :H, c]                              # [nnz, H]
     got_p = got[t, b, H:, c]
@@ -133,7 +134,7 @@ def test_stage_interm(small_case):
     blocks[t, b, :H, c] = SCALE * ref["dS"][t, :, k]
     blocks[t, b, H:, c] = ref["P"][t, :, k]
     bits = orc.f64_to_bf16_rne(blocks)
-    interm = B.smla_interm(d["q"], d["dO"], dev_bf16(bits.reshape(-1)), d["idx"], N)
+    interm = B.smla_interm(d["q"], d["dO"], dev_bf16(dsp_from_logical(bits, H)), d["idx"], N)
     torch.cuda.synchronize()
     got = host_bf16(interm).reshape(T, K, 512)
     blk64 = orc.bf16_to_f64(bits)
