@@ -235,19 +235,23 @@ constexpr int kMinStream = 5;  // segments this long hand over to the next witho
 // d-chunk g, so the four lanes of a quad name four different rows and the L1
 // splits each load into four times as many partial-line accesses (measured on
 // gfx950: about 15 B/clk per CU, from L2 too).  The fragments are therefore
-// loaded with lane 4*c16 + g holding head c16, chunk g (each quad reads 64
-// contiguous bytes of one row: about 50 B/clk) and moved to lane c16 + 16g
-// with one fixed lane permutation per register.  Reading the registers there
+// loaded with lane 4*c16 + p holding head c16 (each quad reads 64 contiguous
+// bytes of one row: about 50 B/clk) and moved to lane c16 + 16g with one fixed
+// lane permutation per register.  Heads 8..15 take their chunks rotated by two
+// within the quad (lane 4*c16 + p holds chunk (p + 2) % 4), so that each half
+// wave of the permutation reads 32 source lanes that are distinct modulo 32:
+// free of LDS bank conflicts (the plain order gives two-way conflicts, about
+// 2 extra cycles per permutation, measured).  Reading the registers there
 // also makes the compiler complete their loads at that point: registers still
 // in flight at a loop's back edge would make it wait, with a vmcnt that also
 // covers every earlier store, at the start of each later iteration.
 __device__ __forceinline__ int frag_load_lane_row(int lane) { return lane >> 2; }
-__device__ __forceinline__ int frag_load_lane_chunk(int lane) { return lane & 3; }
+__device__ __forceinline__ int frag_load_lane_chunk(int lane) { return ((lane & 3) + ((lane >> 4) & 2)) & 3; }
 
 template <int N>
 __device__ __forceinline__ void frag_to_mfma_lanes(u32x4 (&r)[N], int lane) {
-    // destination lane l = c16 + 16g takes source lane 4*c16 + g
-    const int addr = 4 * (4 * (lane & 15) + (lane >> 4));
+    // destination lane l = c16 + 16g takes source lane 4*c16 + (g + 2*(c16 >= 8)) % 4
+    const int addr = 4 * (4 * (lane & 15) + (((lane >> 4) + ((lane >> 2) & 2)) & 3));
 #pragma unroll
     for (int i = 0; i < N; ++i)
 #pragma unroll
