@@ -347,8 +347,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     // forward: lse of the item whose last tile was just produced (or that has no
     // valid slot), with the sink folded in; returns the output scale a/z of the head
     auto finish_softmax = [&]() -> float {
-        float l_tot = l_run + wave_xor(l_run, 16);
-        l_tot += wave_xor(l_tot, 32);
+        const float l_tot = sum_over_rows(l_run);
         const float m_fin = fmaxf(m_use, bias);
         float osc = 0.f, lse_v = -INFINITY;
         if (m_fin != -INFINITY) {
@@ -432,8 +431,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                     x[st][i] = v ? sacc[st][i] * c : -INFINITY;
                     tmax = fmaxf(tmax, x[st][i]);
                 }
-            tmax = fmaxf(tmax, wave_xor(tmax, 16));
-            tmax = fmaxf(tmax, wave_xor(tmax, 32));
+            tmax = max_over_rows(tmax);
             // every tile holds a valid slot, so tmax is finite and the first tile moves
             const bool move = tmax > m_use + kLazy;
             const float m_new = move ? tmax : m_use;

@@ -89,8 +89,7 @@ void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
                     x[st][j] = v ? sacc[st][j] * c : -INFINITY;
                     tmax = fmaxf(tmax, x[st][j]);
                 }
-            tmax = fmaxf(tmax, wave_xor(tmax, 16));
-            tmax = fmaxf(tmax, wave_xor(tmax, 32));
+            tmax = max_over_rows(tmax);
             // every tile holds at least one valid slot, so m_new is finite
             const float m_new = fmaxf(m_run, tmax);
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
@@ -115,9 +114,7 @@ void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
         __syncthreads();
     }
 
-    float l_tot = l_run;
-    l_tot += wave_xor(l_tot, 16);
-    l_tot += wave_xor(l_tot, 32);
+    const float l_tot = sum_over_rows(l_run);
     // fold in the sink: a raw logit (not scaled) with a zero value vector
     const float xs = (sink != nullptr) ? sink[h] * kLog2e : -INFINITY;
     const float m_fin = fmaxf(m_run, xs);

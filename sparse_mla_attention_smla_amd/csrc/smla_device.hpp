@@ -56,6 +56,24 @@ __device__ __forceinline__ T wave_xor(T v, int mask) {
     return __shfl_xor(v, mask, 64);
 }
 
+// Reductions over the four 16-lane rows (lanes l, l^16, l^32, l^48), with the
+// gfx950 row swaps instead of LDS permutes: a 16-row swap of v with itself
+// leaves rows (0,0,2,2) in one result and (1,1,3,3) in the other, a 32-lane
+// swap the halves (lo,lo) and (hi,hi).  Every lane gets the same value; the
+// sum is (v0 + v1) + (v2 + v3) or its mirror, equal bit for bit.
+__device__ __forceinline__ float max_over_rows(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float m = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float m = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 
 // An MFMA accumulator or fragment lane c16 + 16g holds 8 bytes of row c16 at
 // chunk g, so a store in that lane order puts four rows in every quad of
