@@ -269,7 +269,8 @@ def dsp_numel(T, H, topk) -> int:
 
 def smla_dq(q, kv, dO, lse, delta, idx, scale=None, dsp=None, dq=None):
     """Returns (dq bf16 [T,H,512], dsp bf16 blocks): per token, compacted tiles of
-    32 valid slots, each a [2H][32] block (rows scale*dS then P)."""
+    32 valid slots, each a block of 2H x 32 values (rows scale*dS then P) in the
+    piece layout documented with smla_dq in include/smla.h."""
     T, H, _ = q.shape
     N, K = kv.shape[0], idx.shape[1]
     for t, n, dt, sh in ((q, "q", torch.bfloat16, (T, H, D)), (kv, "kv", torch.bfloat16, (N, D)),

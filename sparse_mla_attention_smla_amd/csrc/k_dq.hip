@@ -19,9 +19,11 @@
 // stream and roles, with an online softmax in place of the gradient.
 //
 // dsp layout (consumed by the intermediate kernel): for token t and compacted
-// tile c (c < ceil(topk/32)), a [2H][32] bf16 block at ((t*ceil(topk/32) + c)*2H)*32:
-// rows 0..H-1 hold scale*dS of head h, rows H..2H-1 hold P, column j is the
-// j-th slot of the tile; tail columns past the last valid slot hold zeros.
+// tile c (c < ceil(topk/32)), a block of 2H x 32 bf16 values at
+// ((t*ceil(topk/32) + c)*2H)*32: rows 0..H-1 hold scale*dS of head h, rows
+// H..2H-1 hold P, for the 32 slots of the tile (zeros past the last valid
+// slot).  Each 16-row chunk is 64 pieces of 8 values in MFMA lane order:
+// piece g*16 + r%16 holds slots 4g..4g+3 and 16+4g..16+4g+3 of row r.
 #include <type_traits>
 
 #include "kv_tile.hpp"

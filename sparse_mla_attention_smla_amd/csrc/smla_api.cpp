@@ -123,7 +123,7 @@ smla_status check_shape(int T, int H, int num_kv, int topk) {
 
 smla_status hip_status(hipError_t e) { return e == hipSuccess ? SMLA_OK : SMLA_ERR_HIP; }
 
-// dS/P blocks: per token ceil(topk/32) blocks of [2H][32] bf16
+// dS/P blocks: per token ceil(topk/32) blocks of 2H*32 bf16 (the piece layout of smla.h)
 size_t dsp_bytes(int T, int H, int topk) {
     return (size_t)T * (size_t)((topk + 31) / 32) * 2 * H * 32 * 2;
 }
