@@ -166,3 +166,19 @@ def test_traffic_hash_ignores_comments_only():
     assert bench._code_only(a) == bench._code_only(b)
     assert bench._code_only(a) != bench._code_only(c)
     assert len(bench.kernel_source_hash()) == 16
+
+
+def test_dsp_piece_layout_helpers_match_the_documented_offsets():
+    """The test helpers that read and build dS/P blocks follow the offset formula
+    documented with smla_dq in include/smla.h (host-side index bookkeeping)."""
+    import numpy as np
+    from tests._helpers import dsp_from_logical, dsp_to_logical
+    for H in (16, 48, 128):
+        logical = np.arange(2 * 2 * H * 32).reshape(2, 2 * H, 32)
+        flat = dsp_from_logical(logical, H)
+        for b in range(2):
+            for r in range(2 * H):
+                for j in range(32):
+                    off = (r // 16) * 512 + ((j % 16) // 4 * 16 + r % 16) * 8 + (j // 16) * 4 + j % 4
+                    assert flat[b * 2 * H * 32 + off] == logical[b, r, j]
+        assert np.array_equal(dsp_to_logical(flat, H).reshape(logical.shape), logical)
