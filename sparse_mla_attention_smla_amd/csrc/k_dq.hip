@@ -517,18 +517,6 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     };
     auto consume = [&](int pos) {
         const int cb = cols_base(c16, g);
-        if constexpr (FWD) {
-            // lane c16 + 16g of acc[.][m] belongs to head 16m + c16: apply the
-            // producers' rescale factors before this tile's P is added
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                if (__builtin_amdgcn_readfirstlane(sh.resc[pos & 1][m])) {
-                    const float a = sh.alpha[pos & 1][m][c16];
-#pragma unroll
-                    for (int dt = 0; dt < 8; ++dt) acc[dt][m] *= a;
-                }
-            }
-        }
         u32x4 b[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) b[m] = sh.dsfrag[pos & 1][m][lane];
@@ -537,6 +525,24 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         u32x4 ca[8];
         ca[0] = tile_cols_a(buf, cb, 8 * dq4);
         ca[1] = tile_cols_a(buf, cb, 8 * dq4 + 1);
+        if constexpr (FWD) {
+            // lane c16 + 16g of acc[.][m] belongs to head 16m + c16: apply the
+            // producers' rescale factors before this tile's P is added.  The
+            // four flags are one 16-byte read issued with the operand reads
+            // above, so the check adds no LDS round trip of its own (reading
+            // them first and branching per flag cost the forward 9%).
+            const u32x4 rf = *reinterpret_cast<const u32x4*>(sh.resc[pos & 1]);
+            if (__builtin_amdgcn_readfirstlane(rf[0] | rf[1] | rf[2] | rf[3])) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if (__builtin_amdgcn_readfirstlane(rf[m])) {
+                        const float a = sh.alpha[pos & 1][m][c16];
+#pragma unroll
+                        for (int dt = 0; dt < 8; ++dt) acc[dt][m] *= a;
+                    }
+                }
+            }
+        }
         __builtin_amdgcn_sched_group_barrier(0x100, 4 + 4, 0);
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
@@ -726,7 +732,7 @@ void smla_k7_fwd_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     __shared__ SlotList Lb[2];
     __shared__ u32x4 dsfrag[2][4][64];
     __shared__ __attribute__((aligned(16))) char touch[1024];
-    __shared__ int resc[2][4];
+    __shared__ __attribute__((aligned(16))) int resc[2][4];
     __shared__ float alpha[2][4][16];
     __shared__ float oscale[2][4][16];
     const DqShared sh{tiles, Lb, dsfrag, touch, resc, alpha, oscale};
