@@ -29,8 +29,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_BF16_FLOP_PER_CLK_PER_CU = 4096   # 4 SIMDs x one 16x16x32 bf16 MFMA (16,384 flop) per 16 clocks
 D = 512
 
 
@@ -98,6 +99,34 @@ def stored_traffic(kernel: str):
     return None if k is None else k.get("bytes_per_launch")
 
 
+def device_info():
+    """CU count and peak shader clock of device 0 (hipDeviceGetAttribute through
+    the HIP runtime that torch loaded), and the bf16 MFMA peak they imply."""
+    import ctypes
+
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    cus = int(props.multi_processor_count)
+    clock_khz = None
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (value 5 in hip_runtime_api.h): peak clock in kHz
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0 and 5e5 < v.value < 5e6:
+            clock_khz = int(v.value)
+    except OSError:
+        pass
+    info = {"name": props.name, "arch": props.gcnArchName, "cus": cus,
+            "peak_clock_ghz": None if clock_khz is None else clock_khz / 1e6,
+            "mfma_bf16_flop_per_clk_per_cu": MFMA_BF16_FLOP_PER_CLK_PER_CU}
+    if clock_khz is not None:
+        info["derived_bf16_peak_tflops"] = round(cus * MFMA_BF16_FLOP_PER_CLK_PER_CU * clock_khz * 1e3 / 1e12, 1)
+    info["peak_used_tflops"] = PEAK_BF16_TFLOPS
+    info["peak_note"] = ("fractions divide by the published 2500 TFLOPS dense bf16 peak; "
+                         "derived = CUs x 4096 flop/clk x peak clock")
+    return info
+
+
 def time_graph(w, step, reps):
     """ms per call when one smla_bwd call, captured in a HIP graph on a side stream,
     is replayed (same kernels, same buffers; the graph holds no allocation)."""
@@ -129,7 +158,7 @@ def time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq, dk
     """ms per call of the bounded-workspace backward on the same inputs and outputs."""
     import torch
     T, H, N, K = w.T, w.H, w.num_kv, w.topk
-    ph_ws = torch.empty(B.lib().smla_bwd_phased_workspace_bytes(T, H, N, K, ph_tokens),
+    ph_ws = torch.empty(B.lib().smla_bwd_phased_workspace_bytes(T, H, N, K, ph_tokens, 0),
                         dtype=torch.uint8, device="cuda")
 
     def phased():
@@ -169,19 +198,23 @@ def cpu_baseline(w, n_tokens):
         o_t, l_t = orc.forward_token(orc.bf16_to_f64(x["q"][t]), kv64, x["idx"][t],
                                      x["sink"].astype(np.float64), scale)
         O[t], lse[t] = orc.emit_forward_outputs(o_t, l_t)
-    # timed in chunks of 256 tokens so the oracle's per-token outputs stay small
+    # The whole oracle backward (delta, dq, P/dS, the per-slot intermediate, its
+    # accumulation into dkv, d_sink) on the sampled tokens, timed in chunks of
+    # 256 tokens so that the oracle's per-token outputs stay small.
     dt = 0.0
     for i in range(0, len(toks), 256):
+        tt = toks[i:i + 256]
+        q, dO, Os, ls, ix = x["q"][tt], x["dO"][tt], O[tt], lse[tt], x["idx"][tt]
         t0 = time.perf_counter()
-        orc.backward_tokens(x["q"], x["kv"], x["dO"], O, lse, x["idx"], x["sink"], scale, toks[i:i + 256])
+        orc.backward(q, x["kv"], dO, Os, ls, ix, x["sink"], scale)
         dt += time.perf_counter() - t0
     flops = 10.0 * n_tokens * w.H * w.topk * D
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {
         "value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
-        "sample": f"fp64 NumPy oracle backward (dq, P, dS, interm) on {n_tokens} evenly spaced of "
-                  f"{w.T} tokens of the {w.name} workload; {dt:.2f} s; extrapolated "
-                  f"{dt * w.T / n_tokens * 1e3:.0f} ms per full call",
+        "sample": f"fp64 NumPy oracle backward (delta, dq, P, dS, interm, dkv accumulation, d_sink) "
+                  f"on {n_tokens} evenly spaced of {w.T} tokens of the {w.name} workload; "
+                  f"{dt:.2f} s; extrapolated {dt * w.T / n_tokens * 1e3:.0f} ms per full call",
         "host_cpus": len(os.sched_getaffinity(0)),
     }
 
@@ -204,6 +237,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    dev_info = device_info()
     w = inputs.WORKLOADS[args.workload]
     T, H, N, K = w.T, w.H, w.num_kv, w.topk
     scale = 1.0 / math.sqrt(D)
@@ -386,6 +420,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "frac_of_bf16_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "valid_slot_tflops": round(tflops * nnz / (T * K), 2),
+        "valid_slot_frac_of_bf16_peak": round(tflops * nnz / (T * K) / PEAK_BF16_TFLOPS, 4),
+        "device": dev_info,
         "dtype": "bf16",
         "data": "synthetic (seeded; O and lse from the library forward)",
         "config": {"workload": f"{w.name}: T={T} H={H} D={D} num_kv={N} topk={K}, "

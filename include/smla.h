@@ -26,14 +26,18 @@
  *    ranges must not overlap any other argument (else SMLA_ERR_INVALID_ARG).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    work: they return without synchronising; results are ready when the
- *    stream reaches that point.  smla_bwd also uses one library-owned helper
- *    stream per device (default priority): it forks there with an event
- *    recorded on `stream` and joins back with an event that `stream` waits
- *    on, so all of its results are still ordered on `stream`.  No hipMemset is
- *    enqueued (every output cell is written by a kernel), so calls may be
- *    captured into a HIP graph (the fork/join is the usual captured pattern).
- *    Concurrent smla_bwd calls from several host threads are safe; their
- *    enqueues are serialised.
+ *    stream reaches that point.  An eager smla_bwd / smla_bwd_phased call also
+ *    uses one library-owned helper stream per device (default priority): it
+ *    forks there with an event recorded on `stream` and joins back with an
+ *    event that `stream` waits on, so all of its results are still ordered on
+ *    `stream`.  When `stream` is being captured into a HIP graph, the call
+ *    enqueues every stage on `stream` itself instead (same kernels, same
+ *    results bit for bit), so the helper stream never joins a capture.  No
+ *    hipMemset is enqueued (every output cell is written by a kernel).
+ *    Calls from several host threads are safe, also while another thread
+ *    captures: the library's enqueues are serialised by one mutex, and calls
+ *    on different streams share only the helper stream (their work there runs
+ *    in enqueue order; each call's buffers are its own).
  *  - Argument errors are reported synchronously before anything is enqueued.
  *    SMLA_ERR_ARCH is returned when the current device is not gfx950 (the
  *    page's wrapper likewise refuses other architectures).  A failed launch
@@ -89,8 +93,9 @@ int smla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const fl
 /* Backward                                                                 */
 /* ------------------------------------------------------------------------ */
 
-/* Bytes of workspace smla_bwd needs for this shape (0 on a shape error). */
-size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk);
+/* Bytes of workspace smla_bwd needs for this shape (0 on a shape error or
+ * flags != 0). */
+size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk, uint32_t flags);
 
 /*
  * smla_bwd -- training backward: (dq, dkv, d_sink) from (q, kv, dO, O, lse, idx, sink).
@@ -104,6 +109,8 @@ size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk);
  *             d lse / d sink = P_sink, so it enters as delta -> delta - dlse.
  *   dq  bf16 [T, H, 512] out     dkv bf16 [num_kv, 512] out
  *   d_sink float [H] out; must be non-NULL exactly when sink is non-NULL
+ *   flags     reserved for variants of the op; must be 0 (else
+ *             SMLA_ERR_INVALID_ARG, before anything is enqueued)
  *   n_invalid int32 [1] out or NULL: count of index values that are neither
  *             -1 nor in [0, num_kv)
  *   workspace device scratch of at least smla_bwd_workspace_bytes() bytes,
@@ -116,7 +123,7 @@ size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk);
  */
 int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
              const float* lse, const int32_t* idx, const float* sink, const float* dlse,
-             int T, int H, int num_kv, int topk, float scale,
+             int T, int H, int num_kv, int topk, float scale, uint32_t flags,
              uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
              void* workspace, size_t workspace_bytes, void* stream);
 
@@ -134,12 +141,14 @@ int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
  */
 int smla_bwd_timed(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
                    const float* lse, const int32_t* idx, const float* sink, const float* dlse,
-                   int T, int H, int num_kv, int topk, float scale,
+                   int T, int H, int num_kv, int topk, float scale, uint32_t flags,
                    uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
                    void* workspace, size_t workspace_bytes, void* stream, void* const* events);
 
-/* Bytes of workspace smla_bwd_phased needs (0 on a shape error or phase_tokens < 1). */
-size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int phase_tokens);
+/* Bytes of workspace smla_bwd_phased needs (0 on a shape error, phase_tokens < 1
+ * or flags != 0). */
+size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int phase_tokens,
+                                       uint32_t flags);
 
 /*
  * smla_bwd_phased -- the same backward with a workspace bounded by a token
@@ -148,7 +157,8 @@ size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int p
  * blocks, the intermediate, the inverted index and the gather scratch hold
  * phase_tokens tokens at a time, and dkv is carried across phases as an fp32
  * running sum (num_kv * 2 KiB of workspace) that is rounded to bf16 once.
- *   phase_tokens >= 1 (else SMLA_ERR_SHAPE); all other arguments as smla_bwd.
+ *   phase_tokens >= 1 (else SMLA_ERR_SHAPE); all other arguments (flags
+ *   included) as smla_bwd.
  * Phases run in token order; each phase's inverted index is built on the
  * helper stream while dQ and the intermediate of that phase run (the same
  * fork/join pattern as smla_bwd).  With
@@ -157,7 +167,7 @@ size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int p
  */
 int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
                     const float* lse, const int32_t* idx, const float* sink, const float* dlse,
-                    int T, int H, int num_kv, int topk, float scale, int phase_tokens,
+                    int T, int H, int num_kv, int topk, float scale, uint32_t flags, int phase_tokens,
                     uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
                     void* workspace, size_t workspace_bytes, void* stream);
 

@@ -10,6 +10,7 @@ smla_delta, smla_dq, smla_interm, smla_build_csr, smla_gather, smla_dsink.
 """
 from __future__ import annotations
 
+import collections
 import ctypes
 import math
 import os
@@ -28,17 +29,18 @@ _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
 _Z = ctypes.c_size_t
+_U = ctypes.c_uint32
 
 _SIGNATURES = {
     "smla_status_string": ([_I], ctypes.c_char_p),
     "smla_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
-    "smla_bwd_workspace_bytes": ([_I, _I, _I, _I], _Z),
-    "smla_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
-    "smla_bwd_timed": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P, _P, _P, _Z, _P,
-                        _P], _I),
-    "smla_bwd_phased_workspace_bytes": ([_I, _I, _I, _I, _I], _Z),
-    "smla_bwd_phased": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _P, _P, _P, _P, _Z,
-                         _P], _I),
+    "smla_bwd_workspace_bytes": ([_I, _I, _I, _I, _U], _Z),
+    "smla_bwd": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "smla_bwd_timed": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P, _P, _P, _P, _Z,
+                        _P, _P], _I),
+    "smla_bwd_phased_workspace_bytes": ([_I, _I, _I, _I, _I, _U], _Z),
+    "smla_bwd_phased": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _I, _P, _P, _P, _P, _P,
+                         _Z, _P], _I),
     "smla_delta": ([_P, _P, _P, _I, _I, _P, _P], _I),
     "smla_dq": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "smla_interm": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
@@ -95,15 +97,28 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _need(t, name, dtype, shape=None):
+def _need(t, name, dtype, shape=None, device=None):
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise TypeError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if shape is not None and tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(ws, name, device, need=None):
+    """Check a caller-given workspace (contiguous uint8 on `device`, at least
+    `need` bytes when given); returns its size in bytes, which is what the C
+    entry point is told (so that its own size check sees the real buffer)."""
+    _need(ws, name, torch.uint8, device=device)
+    n = ws.numel() * ws.element_size()
+    if need is not None and n < need:
+        raise ValueError(f"{name} holds {n} bytes, {need} are needed")
+    return n
 
 
 def _default_scale(scale):
@@ -129,33 +144,85 @@ def smla_fwd(q, kv, idx, sink=None, scale=None, out=None):
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
     else:
         o, lse = out
-        _need(o, "o", torch.bfloat16, (T, H, D))
-        _need(lse, "lse", torch.float32, (T, H))
+        _need(o, "o", torch.bfloat16, (T, H, D), q.device)
+        _need(lse, "lse", torch.float32, (T, H), q.device)
     _check("smla_fwd", lib().smla_fwd(_ptr(q), _ptr(kv), _ptr(idx), _ptr(sink), T, H, N, K,
                                       _default_scale(scale), _ptr(o), _ptr(lse), _stream(q.device)))
     return o, lse
 
 
 def bwd_workspace_bytes(T, H, num_kv, topk) -> int:
-    n = lib().smla_bwd_workspace_bytes(T, H, num_kv, topk)
+    n = lib().smla_bwd_workspace_bytes(T, H, num_kv, topk, 0)
     if n == 0:
         raise SmlaError("smla_bwd_workspace_bytes", 2)
     return n
 
 
-_ws_cache: dict = {}
+_WS_CACHE_MAX = 2
+_ws_cache: "collections.OrderedDict" = collections.OrderedDict()
+_ws_lock = threading.Lock()
 
 
 def bwd_workspace(T, H, num_kv, topk, device):
     """A cached workspace buffer for this shape, device and current stream.  Calls
     on one stream run in order and may share it; a call on another stream (say,
-    from another host thread) gets its own, so concurrent calls never share one."""
+    from another host thread) gets its own, so concurrent calls never share one.
+    At most two buffers are kept (least recently used evicted first); an evicted
+    buffer returns to torch's allocator on the stream it was made for, so work
+    still queued there finishes before the memory is reused."""
     key = (T, H, num_kv, topk, str(device), torch.cuda.current_stream(device).cuda_stream)
-    ws = _ws_cache.get(key)
-    if ws is None:
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is not None:
+            _ws_cache.move_to_end(key)
+            return ws
+        while len(_ws_cache) >= _WS_CACHE_MAX:
+            _ws_cache.popitem(last=False)
         ws = torch.empty(bwd_workspace_bytes(T, H, num_kv, topk), dtype=torch.uint8, device=device)
         _ws_cache[key] = ws
-    return ws
+        return ws
+
+
+def clear_workspace_cache():
+    """Drop every cached backward workspace."""
+    with _ws_lock:
+        _ws_cache.clear()
+
+
+def _bwd_outputs(q, kv, H, sink, out):
+    """Preallocated (dq, dkv, d_sink) checked like the inputs, or new tensors."""
+    T = q.shape[0]
+    N = kv.shape[0]
+    if out is None:
+        dq = torch.empty_like(q)
+        dkv = torch.empty_like(kv)
+        d_sink = torch.empty((H,), dtype=torch.float32, device=q.device) if sink is not None else None
+        return dq, dkv, d_sink
+    dq, dkv, d_sink = out
+    _need(dq, "dq", torch.bfloat16, (T, H, D), q.device)
+    _need(dkv, "dkv", torch.bfloat16, (N, D), q.device)
+    if (sink is None) != (d_sink is None):
+        raise ValueError("out: d_sink must be given exactly when sink is")
+    if d_sink is not None:
+        _need(d_sink, "d_sink", torch.float32, (H,), q.device)
+    return dq, dkv, d_sink
+
+
+def _check_bwd_inputs(q, kv, dO, o, lse, idx, sink, dlse):
+    T, H, _ = q.shape
+    N, K = kv.shape[0], idx.shape[1]
+    dv = q.device
+    _need(q, "q", torch.bfloat16, (T, H, D))
+    _need(kv, "kv", torch.bfloat16, (N, D), dv)
+    _need(dO, "dO", torch.bfloat16, (T, H, D), dv)
+    _need(o, "o", torch.bfloat16, (T, H, D), dv)
+    _need(lse, "lse", torch.float32, (T, H), dv)
+    _need(idx, "idx", torch.int32, (T, K), dv)
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (H,), dv)
+    if dlse is not None:
+        _need(dlse, "dlse", torch.float32, (T, H), dv)
+    return T, H, N, K
 
 
 def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=None,
@@ -168,30 +235,15 @@ def smla_bwd(q, kv, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=
     call records on its stream at the stage boundaries (smla_bwd_timed): before
     delta and after delta, dQ, the intermediate and the gather.
     """
-    T, H, _ = q.shape
-    N, K = kv.shape[0], idx.shape[1]
-    _need(q, "q", torch.bfloat16, (T, H, D))
-    _need(kv, "kv", torch.bfloat16, (N, D))
-    _need(dO, "dO", torch.bfloat16, (T, H, D))
-    _need(o, "o", torch.bfloat16, (T, H, D))
-    _need(lse, "lse", torch.float32, (T, H))
-    _need(idx, "idx", torch.int32, (T, K))
-    if sink is not None:
-        _need(sink, "sink", torch.float32, (H,))
-    if dlse is not None:
-        _need(dlse, "dlse", torch.float32, (T, H))
-    if out is None:
-        dq = torch.empty_like(q)
-        dkv = torch.empty_like(kv)
-        d_sink = torch.empty((H,), dtype=torch.float32, device=q.device) if sink is not None else None
-    else:
-        dq, dkv, d_sink = out
+    T, H, N, K = _check_bwd_inputs(q, kv, dO, o, lse, idx, sink, dlse)
+    dq, dkv, d_sink = _bwd_outputs(q, kv, H, sink, out)
     if workspace is None:
         workspace = bwd_workspace(T, H, N, K, q.device)
+    ws_bytes = _workspace(workspace, "workspace", q.device)
     n_inv = torch.empty((1,), dtype=torch.int32, device=q.device) if count_invalid else None
     args = (_ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
-            _default_scale(scale), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
-            _ptr(workspace), workspace.numel(), _stream(q.device))
+            _default_scale(scale), 0, _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
+            _ptr(workspace), ws_bytes, _stream(q.device))
     if events is None:
         _check("smla_bwd", lib().smla_bwd(*args))
     else:
@@ -211,34 +263,19 @@ def smla_bwd_phased(q, kv, dO, o, lse, idx, sink=None, scale=None, phase_tokens=
                     out=None, count_invalid=False, dlse=None):
     """The backward with a workspace bounded by `phase_tokens` tokens: returns
     (dq, dkv, d_sink[, n_invalid]) like smla_bwd."""
-    T, H, _ = q.shape
-    N, K = kv.shape[0], idx.shape[1]
-    _need(q, "q", torch.bfloat16, (T, H, D))
-    _need(kv, "kv", torch.bfloat16, (N, D))
-    _need(dO, "dO", torch.bfloat16, (T, H, D))
-    _need(o, "o", torch.bfloat16, (T, H, D))
-    _need(lse, "lse", torch.float32, (T, H))
-    _need(idx, "idx", torch.int32, (T, K))
-    if sink is not None:
-        _need(sink, "sink", torch.float32, (H,))
-    if dlse is not None:
-        _need(dlse, "dlse", torch.float32, (T, H))
-    if out is None:
-        dq = torch.empty_like(q)
-        dkv = torch.empty_like(kv)
-        d_sink = torch.empty((H,), dtype=torch.float32, device=q.device) if sink is not None else None
-    else:
-        dq, dkv, d_sink = out
+    T, H, N, K = _check_bwd_inputs(q, kv, dO, o, lse, idx, sink, dlse)
+    dq, dkv, d_sink = _bwd_outputs(q, kv, H, sink, out)
     if workspace is None:
-        n = lib().smla_bwd_phased_workspace_bytes(T, H, N, K, int(phase_tokens))
+        n = lib().smla_bwd_phased_workspace_bytes(T, H, N, K, int(phase_tokens), 0)
         if n == 0:
             raise SmlaError("smla_bwd_phased_workspace_bytes", 2)
         workspace = torch.empty((n,), dtype=torch.uint8, device=q.device)
+    ws_bytes = _workspace(workspace, "workspace", q.device)
     n_inv = torch.empty((1,), dtype=torch.int32, device=q.device) if count_invalid else None
     _check("smla_bwd_phased", lib().smla_bwd_phased(
         _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
-        _default_scale(scale), int(phase_tokens), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
-        _ptr(workspace), workspace.numel(), _stream(q.device)))
+        _default_scale(scale), 0, int(phase_tokens), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
+        _ptr(workspace), ws_bytes, _stream(q.device)))
     if count_invalid:
         return dq, dkv, d_sink, n_inv
     return dq, dkv, d_sink
@@ -257,6 +294,8 @@ def smla_delta(o, dO, delta=None, dlse=None):
         _need(dlse, "dlse", torch.float32, (T, H))
     if delta is None:
         delta = torch.empty((T, H), dtype=torch.float32, device=o.device)
+    else:
+        _need(delta, "delta", torch.float32, (T, H), o.device)
     _check("smla_delta", lib().smla_delta(_ptr(o), _ptr(dO), _ptr(dlse), T, H, _ptr(delta),
                                           _stream(o.device)))
     return delta
@@ -279,8 +318,12 @@ def smla_dq(q, kv, dO, lse, delta, idx, scale=None, dsp=None, dq=None):
         _need(t, n, dt, sh)
     if dq is None:
         dq = torch.empty_like(q)
+    else:
+        _need(dq, "dq", torch.bfloat16, (T, H, D), q.device)
     if dsp is None:
         dsp = torch.empty((dsp_numel(T, H, K),), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(dsp, "dsp", torch.bfloat16, (dsp_numel(T, H, K),), q.device)
     _check("smla_dq", lib().smla_dq(_ptr(q), _ptr(kv), _ptr(dO), _ptr(lse), _ptr(delta), _ptr(idx),
                                     T, H, N, K, _default_scale(scale), _ptr(dq), _ptr(dsp),
                                     _stream(q.device)))
@@ -296,6 +339,8 @@ def smla_interm(q, dO, dsp, idx, num_kv, interm=None):
     _need(idx, "idx", torch.int32, (T, K))
     if interm is None:
         interm = torch.empty((T * K, D), dtype=torch.bfloat16, device=q.device)
+    else:
+        _need(interm, "interm", torch.bfloat16, (T * K, D), q.device)
     _check("smla_interm", lib().smla_interm(_ptr(q), _ptr(dO), _ptr(dsp), _ptr(idx), T, H, num_kv, K,
                                             _ptr(interm), _stream(q.device)))
     return interm
@@ -310,40 +355,53 @@ def smla_build_csr(idx, num_kv, count_invalid=False, out=None, workspace=None):
         slots = torch.empty((max(T * K, 1),), dtype=torch.int32, device=idx.device)
     else:
         row_ptr, slots = out
+        _need(row_ptr, "row_ptr", torch.int32, (num_kv + 1,), idx.device)
+        _need(slots, "slots", torch.int32, None, idx.device)
+        if slots.numel() < T * K:
+            raise ValueError(f"slots holds {slots.numel()} entries, T*topk = {T * K} are needed")
     n = lib().smla_csr_workspace_bytes(T, K, num_kv)
     if n == 0:
         raise SmlaError("smla_csr_workspace_bytes", 2)
     ws = torch.empty((n,), dtype=torch.uint8, device=idx.device) if workspace is None else workspace
+    ws_bytes = _workspace(ws, "workspace", idx.device)
     n_inv = torch.empty((1,), dtype=torch.int32, device=idx.device) if count_invalid else None
     _check("smla_build_csr", lib().smla_build_csr(_ptr(idx), T, K, num_kv, _ptr(row_ptr), _ptr(slots),
-                                                  _ptr(n_inv), _ptr(ws), n, _stream(idx.device)))
+                                                  _ptr(n_inv), _ptr(ws), ws_bytes, _stream(idx.device)))
     return (row_ptr, slots, n_inv) if count_invalid else (row_ptr, slots)
 
 
 def smla_gather(interm, row_ptr, slots, T, topk, num_kv, dkv=None, workspace=None):
+    dv = interm.device
     _need(interm, "interm", torch.bfloat16, (T * topk, D))
-    _need(row_ptr, "row_ptr", torch.int32, (num_kv + 1,))
-    _need(slots, "slots", torch.int32)
+    _need(row_ptr, "row_ptr", torch.int32, (num_kv + 1,), dv)
+    _need(slots, "slots", torch.int32, None, dv)
     if dkv is None:
-        dkv = torch.empty((num_kv, D), dtype=torch.bfloat16, device=interm.device)
+        dkv = torch.empty((num_kv, D), dtype=torch.bfloat16, device=dv)
+    else:
+        _need(dkv, "dkv", torch.bfloat16, (num_kv, D), dv)
     n = lib().smla_gather_workspace_bytes(T, topk, num_kv)
     if n == 0:
         raise SmlaError("smla_gather_workspace_bytes", 2)
-    ws = torch.empty((n,), dtype=torch.uint8, device=interm.device) if workspace is None else workspace
+    ws = torch.empty((n,), dtype=torch.uint8, device=dv) if workspace is None else workspace
+    ws_bytes = _workspace(ws, "workspace", dv)
     _check("smla_gather", lib().smla_gather(_ptr(interm), _ptr(row_ptr), _ptr(slots), T, topk, num_kv,
-                                            _ptr(dkv), _ptr(ws), n, _stream(interm.device)))
+                                            _ptr(dkv), _ptr(ws), ws_bytes, _stream(dv)))
     return dkv
 
 
 def smla_dsink(lse, delta, sink, d_sink=None, workspace=None):
     T, H = lse.shape
+    dv = lse.device
     _need(lse, "lse", torch.float32, (T, H))
-    _need(delta, "delta", torch.float32, (T, H))
-    _need(sink, "sink", torch.float32, (H,))
+    _need(delta, "delta", torch.float32, (T, H), dv)
+    _need(sink, "sink", torch.float32, (H,), dv)
     if d_sink is None:
-        d_sink = torch.empty((H,), dtype=torch.float32, device=lse.device)
+        d_sink = torch.empty((H,), dtype=torch.float32, device=dv)
+    else:
+        _need(d_sink, "d_sink", torch.float32, (H,), dv)
     n = lib().smla_dsink_workspace_bytes(T, H)
-    ws = torch.empty((max(n, 4),), dtype=torch.uint8, device=lse.device) if workspace is None else workspace
+    ws = torch.empty((max(n, 4),), dtype=torch.uint8, device=dv) if workspace is None else workspace
+    ws_bytes = _workspace(ws, "workspace", dv)
     _check("smla_dsink", lib().smla_dsink(_ptr(lse), _ptr(delta), _ptr(sink), T, H, _ptr(d_sink),
-                                          _ptr(ws), n, _stream(lse.device)))
+                                          _ptr(ws), ws_bytes, _stream(dv)))
     return d_sink

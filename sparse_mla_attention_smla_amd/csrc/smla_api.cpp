@@ -77,6 +77,7 @@ SideStream g_side[kMaxDevices];
 std::mutex g_side_mu;
 
 SideStream* side_stream(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
     SideStream& d = g_side[dev];
     if (d.state == 0) {
         d.state = 2;
@@ -88,6 +89,18 @@ SideStream* side_stream(int dev) {
             d.state = 1;
     }
     return d.state == 1 ? &d : nullptr;
+}
+
+// The helper stream for a call on `s`, or nullptr when `s` is being captured
+// into a graph: then every stage is enqueued on `s` itself, so no
+// library-owned stream ever joins a capture (and eager calls from other
+// threads keep using the helper stream while the capture is open).  *err is
+// set when the capture state cannot be read.
+SideStream* side_for(hipStream_t s, int dev, bool* err) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    *err = hipStreamIsCapturing(s, &cs) != hipSuccess;
+    if (*err || cs != hipStreamCaptureStatusNone) return nullptr;
+    return side_stream(dev);
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -207,13 +220,14 @@ const char* smla_status_string(int status) {
     }
 }
 
-size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk) {
-    if (check_shape(T, H, num_kv, topk) != SMLA_OK) return 0;
+size_t smla_bwd_workspace_bytes(int T, int H, int num_kv, int topk, uint32_t flags) {
+    if (flags != 0 || check_shape(T, H, num_kv, topk) != SMLA_OK) return 0;
     return bwd_layout(T, H, num_kv, topk).total;
 }
 
-size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int phase_tokens) {
-    if (check_shape(T, H, num_kv, topk) != SMLA_OK || phase_tokens < 1) return 0;
+size_t smla_bwd_phased_workspace_bytes(int T, int H, int num_kv, int topk, int phase_tokens,
+                                       uint32_t flags) {
+    if (flags != 0 || check_shape(T, H, num_kv, topk) != SMLA_OK || phase_tokens < 1) return 0;
     return phased_layout(T, H, num_kv, topk, phase_tokens).total;
 }
 
@@ -264,12 +278,12 @@ namespace {
 // caller's stream before delta and after delta, dQ, the intermediate and the gather.
 int bwd_impl(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
              const float* lse, const int32_t* idx, const float* sink, const float* dlse, int T,
-             int H, int num_kv, int topk, float scale, uint16_t* dq, uint16_t* dkv, float* d_sink,
-             int32_t* n_invalid, void* workspace, size_t workspace_bytes, void* stream,
-             void* const* ev) {
+             int H, int num_kv, int topk, float scale, uint32_t flags, uint16_t* dq, uint16_t* dkv,
+             float* d_sink, int32_t* n_invalid, void* workspace, size_t workspace_bytes,
+             void* stream, void* const* ev) {
     smla_status st = check_shape(T, H, num_kv, topk);
     if (st != SMLA_OK) return st;
-    if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+    if (flags != 0 || !std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
     if (!kv || !dkv) return SMLA_ERR_INVALID_ARG;
     if (T > 0 && (!q || !dO || !o || !lse || !idx || !dq)) return SMLA_ERR_INVALID_ARG;
     if ((sink == nullptr) != (d_sink == nullptr)) return SMLA_ERR_INVALID_ARG;
@@ -313,11 +327,14 @@ int bwd_impl(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_side_mu);
-    SideStream* side = side_stream(dev);
+    bool cap_err = false;
+    SideStream* side = side_for(s, dev, &cap_err);
+    if (cap_err) return SMLA_ERR_HIP;
     // The CSR and the gather plan depend only on the indices, d_sink only on
     // lse and delta: they run on the helper stream while dQ and the
     // intermediate run on the caller's stream (all in one order on the
-    // caller's stream when no helper stream could be made).
+    // caller's stream under graph capture, or when no helper stream could be
+    // made).
     hipStream_t aux = side != nullptr ? side->s : s;
     if (side != nullptr) {
         if (hipEventRecord(side->fork, s) != hipSuccess ||
@@ -358,33 +375,34 @@ extern "C" {
 
 int smla_bwd(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
              const float* lse, const int32_t* idx, const float* sink, const float* dlse, int T,
-             int H, int num_kv, int topk, float scale, uint16_t* dq, uint16_t* dkv, float* d_sink,
-             int32_t* n_invalid, void* workspace, size_t workspace_bytes, void* stream) {
-    return bwd_impl(q, kv, dO, o, lse, idx, sink, dlse, T, H, num_kv, topk, scale, dq, dkv, d_sink,
-                    n_invalid, workspace, workspace_bytes, stream, nullptr);
+             int H, int num_kv, int topk, float scale, uint32_t flags, uint16_t* dq, uint16_t* dkv,
+             float* d_sink, int32_t* n_invalid, void* workspace, size_t workspace_bytes,
+             void* stream) {
+    return bwd_impl(q, kv, dO, o, lse, idx, sink, dlse, T, H, num_kv, topk, scale, flags, dq, dkv,
+                    d_sink, n_invalid, workspace, workspace_bytes, stream, nullptr);
 }
 
 int smla_bwd_timed(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
                    const float* lse, const int32_t* idx, const float* sink, const float* dlse,
-                   int T, int H, int num_kv, int topk, float scale, uint16_t* dq, uint16_t* dkv,
-                   float* d_sink, int32_t* n_invalid, void* workspace, size_t workspace_bytes,
-                   void* stream, void* const* events) {
+                   int T, int H, int num_kv, int topk, float scale, uint32_t flags, uint16_t* dq,
+                   uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* workspace,
+                   size_t workspace_bytes, void* stream, void* const* events) {
     if (events == nullptr) return SMLA_ERR_INVALID_ARG;
     for (int i = 0; i < 5; ++i)
         if (events[i] == nullptr) return SMLA_ERR_INVALID_ARG;
-    return bwd_impl(q, kv, dO, o, lse, idx, sink, dlse, T, H, num_kv, topk, scale, dq, dkv, d_sink,
-                    n_invalid, workspace, workspace_bytes, stream, events);
+    return bwd_impl(q, kv, dO, o, lse, idx, sink, dlse, T, H, num_kv, topk, scale, flags, dq, dkv,
+                    d_sink, n_invalid, workspace, workspace_bytes, stream, events);
 }
 
 int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
                     const float* lse, const int32_t* idx, const float* sink, const float* dlse,
-                    int T, int H, int num_kv, int topk, float scale, int phase_tokens, uint16_t* dq,
-                    uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* workspace,
+                    int T, int H, int num_kv, int topk, float scale, uint32_t flags, int phase_tokens,
+                    uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* workspace,
                     size_t workspace_bytes, void* stream) {
     smla_status st = check_shape(T, H, num_kv, topk);
     if (st != SMLA_OK) return st;
     if (phase_tokens < 1) return SMLA_ERR_SHAPE;
-    if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+    if (flags != 0 || !std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
     if (!kv || !dkv) return SMLA_ERR_INVALID_ARG;
     if (T > 0 && (!q || !dO || !o || !lse || !idx || !dq)) return SMLA_ERR_INVALID_ARG;
     if ((sink == nullptr) != (d_sink == nullptr)) return SMLA_ERR_INVALID_ARG;
@@ -435,7 +453,9 @@ int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, c
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_side_mu);
-    SideStream* side = side_stream(dev);
+    bool cap_err = false;
+    SideStream* side = side_for(s, dev, &cap_err);
+    if (cap_err) return SMLA_ERR_HIP;
     hipStream_t aux = side != nullptr ? side->s : s;
     auto rec_wait = [&](hipEvent_t e, hipStream_t from, hipStream_t to) {
         return side == nullptr ||

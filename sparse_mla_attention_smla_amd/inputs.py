@@ -77,6 +77,11 @@ WORKLOADS = {
     # the page's correctness runs also use H = 64
     "headline_h64": Workload("headline_h64", 5, T=4096, H=64, num_kv=5120, topk=512,
                              selection="swa_pool", window=128, pool_stride=4, pool_picks=384),
+    # mid-size parity case: 640 items of 64 heads (several per persistent
+    # workgroup on 256 compute units) and tokens of 1 to 14 tiles of 32 slots
+    # (pool of stride 1, so late tokens see up to 320 pool rows)
+    "mid": Workload("mid", 6, T=320, H=128, num_kv=640, topk=512,
+                    selection="swa_pool", window=128, pool_stride=1, pool_picks=384),
 }
 
 

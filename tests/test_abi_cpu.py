@@ -54,31 +54,35 @@ def test_status_strings(lib):
 
 def test_workspace_sizes(lib):
     # headline shape: delta 2 MiB + dS/P 1 GiB + interm 2 GiB + CSR/gather scratch
-    n = lib.smla_bwd_workspace_bytes(4096, 128, 5120, 512)
+    n = lib.smla_bwd_workspace_bytes(4096, 128, 5120, 512, 0)
     assert 3.0 * 2 ** 30 < n < 3.2 * 2 ** 30
-    assert lib.smla_bwd_workspace_bytes(64, 24, 64, 16) == 0          # H % 16 != 0
-    assert lib.smla_bwd_workspace_bytes(64, 16, 63, 16) == 0          # num_kv < T
+    assert lib.smla_bwd_workspace_bytes(64, 24, 64, 16, 0) == 0          # H % 16 != 0
+    assert lib.smla_bwd_workspace_bytes(64, 16, 63, 16, 0) == 0          # num_kv < T
     assert lib.smla_csr_workspace_bytes(64, 16, 64) > 0
     assert lib.smla_gather_workspace_bytes(64, 16, 64) > 0
     assert lib.smla_dsink_workspace_bytes(64, 16) == 2 * 16 * 4
+    # the reserved flags word: any nonzero value makes the query return 0
+    assert lib.smla_bwd_workspace_bytes(4096, 128, 5120, 512, 1) == 0
+    assert lib.smla_bwd_workspace_bytes(64, 16, 64, 16, 1 << 31) == 0
+    assert lib.smla_bwd_phased_workspace_bytes(64, 16, 64, 16, 16, 4) == 0
     # phased: bounded by the phase, plus an fp32 running dkv (num_kv * 2 KiB)
-    full = lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 4096)
-    part = lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 512)
+    full = lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 4096, 0)
+    part = lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 512, 0)
     assert part < full / 6 and full > n
-    assert lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 10 ** 6) == full
-    assert lib.smla_bwd_phased_workspace_bytes(64, 16, 64, 16, 0) == 0
+    assert lib.smla_bwd_phased_workspace_bytes(4096, 128, 5120, 512, 10 ** 6, 0) == full
+    assert lib.smla_bwd_phased_workspace_bytes(64, 16, 64, 16, 0, 0) == 0
 
 
 A = 0x10000000  # fake, 256-B aligned device addresses (never dereferenced)
 
 
-def _bwd(lib, T=64, H=16, N=64, K=16, scale=0.05, sink=True, d_sink=True, ws=1 << 34, **ptr):
+def _bwd(lib, T=64, H=16, N=64, K=16, scale=0.05, sink=True, d_sink=True, ws=1 << 34, flags=0, **ptr):
     p = dict(q=A, kv=2 * A, dO=3 * A, o=4 * A, lse=5 * A, idx=6 * A, sink=7 * A if sink else None,
              dlse=None, dq=8 * A, dkv=9 * A, d_sink=10 * A if d_sink else None, n_inv=None, work=11 * A)
     p.update(ptr)
     return lib.smla_bwd(p["q"], p["kv"], p["dO"], p["o"], p["lse"], p["idx"], p["sink"], p["dlse"],
                         T, H, N, K,
-                        scale, p["dq"], p["dkv"], p["d_sink"], p["n_inv"], p["work"], ws, None)
+                        scale, flags, p["dq"], p["dkv"], p["d_sink"], p["n_inv"], p["work"], ws, None)
 
 
 def test_bwd_argument_errors(lib):
@@ -86,11 +90,13 @@ def test_bwd_argument_errors(lib):
     assert _bwd(lib, H=144) == SHAPE
     assert _bwd(lib, K=0) == SHAPE
     assert _bwd(lib, T=1, N=64, K=(1 << 20) + 16) == SHAPE    # topk past the 32-bit row offsets
-    assert lib.smla_bwd_workspace_bytes(1, 16, 64, (1 << 20) + 16) == 0
+    assert lib.smla_bwd_workspace_bytes(1, 16, 64, (1 << 20) + 16, 0) == 0
     assert _bwd(lib, N=63) == SHAPE                       # num_kv < T
     assert _bwd(lib, N=1 << 20) == SHAPE
     assert _bwd(lib, T=1 << 20, N=1 << 20 - 1, K=4096) == SHAPE
     assert _bwd(lib, scale=float("nan")) == INVALID
+    assert _bwd(lib, flags=1) == INVALID                  # reserved flags must be 0
+    assert _bwd(lib, flags=1 << 31) == INVALID
     assert _bwd(lib, d_sink=False) == INVALID             # sink without d_sink
     assert _bwd(lib, sink=False) == INVALID               # d_sink without sink
     assert _bwd(lib, q=None) == INVALID
@@ -109,7 +115,7 @@ def test_bwd_argument_errors(lib):
 
 def test_timed_bwd_argument_errors(lib):
     import ctypes
-    p = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, None, 64, 16, 64, 16, 0.05,
+    p = [A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A, 7 * A, None, 64, 16, 64, 16, 0.05, 0,
          8 * A, 9 * A, 10 * A, None, 11 * A, 1 << 34, None]
     assert lib.smla_bwd_timed(*p, None) == INVALID                       # no event array
     evs = (ctypes.c_void_p * 5)(1, 2, None, 4, 5)
@@ -118,17 +124,21 @@ def test_timed_bwd_argument_errors(lib):
     bad = list(p)
     bad[10] = 63                                                         # num_kv < T
     assert lib.smla_bwd_timed(*bad, full) == SHAPE
+    bad = list(p)
+    bad[13] = 2                                                          # reserved flags
+    assert lib.smla_bwd_timed(*bad, full) == INVALID
 
 
 def test_phased_argument_errors(lib):
-    def call(phase=16, ws=1 << 34, **kw):
+    def call(phase=16, ws=1 << 34, flags=0, **kw):
         p = dict(q=A, kv=2 * A, dO=3 * A, o=4 * A, lse=5 * A, idx=6 * A, sink=7 * A, dlse=None,
                  dq=8 * A, dkv=9 * A, d_sink=10 * A, n_inv=None, work=11 * A)
         p.update(kw)
         return lib.smla_bwd_phased(p["q"], p["kv"], p["dO"], p["o"], p["lse"], p["idx"], p["sink"],
-                                   p["dlse"], 64, 16, 64, 16, 0.05, phase, p["dq"], p["dkv"],
+                                   p["dlse"], 64, 16, 64, 16, 0.05, flags, phase, p["dq"], p["dkv"],
                                    p["d_sink"], p["n_inv"], p["work"], ws, None)
     assert call(phase=0) == SHAPE
+    assert call(flags=8) == INVALID
     assert call(ws=1024) == WORKSPACE
     assert call(d_sink=None) == INVALID
     assert call(dkv=A) == INVALID                          # dkv aliases q

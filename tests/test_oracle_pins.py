@@ -417,6 +417,57 @@ def test_sampled_helpers_agree_with_full_backward():
 
 
 # --------------------------------------------------------------------------
+# the gather phase on its own: dkv from a given intermediate
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [8, 16])
+def test_dkv_from_interm_equals_the_finite_difference_pinned_dkv(D):
+    """Gathering the oracle's own per-slot intermediate must give the dkv that
+    central finite differences pin (test_backward_matches_central_differences):
+    the index set there has a duplicate index within a row, -1 padding, an
+    all-masked row and out-of-range values."""
+    for with_sink in (True, False):
+        q, kv, dO, idx, sink, scale = _fd_case(D, with_sink, seed=11 + D + with_sink)
+        O, lse = orc.forward(q, kv, idx, sink, scale)
+        g = orc.backward(q, kv, dO, O, lse, idx, sink, scale, stages=True)
+        got = orc.dkv_from_interm(g["interm"], idx, kv.shape[0])
+        np.testing.assert_allclose(got, g["dkv"], rtol=1e-13, atol=1e-15)
+
+
+def test_dkv_from_interm_brute_force():
+    """Against a plain loop over slots, on arbitrary values: duplicate indices add
+    both rows, -1 and out-of-range indices are dropped, rows nobody addresses are
+    exactly zero.  Also through the bf16 bit-pattern input the GPU tests pass."""
+    rng = np.random.default_rng(41)
+    idx = np.array([[3, -1, 0, 3], [6, 0, 9, -1], [-7, 2, 2, 6], [1, 1, 1, 1], [-1, -1, -1, -1]])
+    N, Dh = 8, 5
+    T, K = idx.shape
+    interm = rng.standard_normal((T, K, Dh))
+    want = np.zeros((N, Dh))
+    for t in range(T):
+        for k in range(K):
+            j = idx[t, k]
+            if 0 <= j < N:
+                want[j] += interm[t, k]
+    got = orc.dkv_from_interm(interm, idx, N)
+    np.testing.assert_allclose(got, want, rtol=1e-15, atol=0)
+    assert np.all(got[[4, 5, 7]] == 0.0)                   # never addressed
+    np.testing.assert_allclose(got[1], interm[3].sum(axis=0), rtol=1e-15)   # four duplicates
+    # a row's slot order does not matter; masked slots carry arbitrary values
+    perm = rng.permutation(K)
+    np.testing.assert_allclose(orc.dkv_from_interm(interm[:, perm], idx[:, perm], N), want, rtol=1e-14)
+    # bf16 bit patterns are decoded exactly before summing
+    bits = orc.f64_to_bf16_rne(interm)
+    dec = orc.bf16_to_f64(bits)
+    want_b = np.zeros((N, Dh))
+    for t in range(T):
+        for k in range(K):
+            if 0 <= idx[t, k] < N:
+                want_b[idx[t, k]] += dec[t, k]
+    np.testing.assert_allclose(orc.dkv_from_interm(bits, idx, N), want_b, rtol=1e-15, atol=0)
+
+
+# --------------------------------------------------------------------------
 # CSR
 # --------------------------------------------------------------------------
 
