@@ -171,6 +171,31 @@ int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, c
                     uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * smla_bwd_noalloc -- the backward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): it takes no workspace and allocates nothing.  Its
+ * workspace is a fixed 256 MiB device array inside the library (one copy per
+ * GPU, held from the library's first use on that GPU until the process ends).
+ *   Arguments as smla_bwd, without workspace/workspace_bytes.
+ * It runs smla_bwd_phased with the largest token phase whose workspace fits
+ * the array, every stage on `stream` (no helper stream), so its results equal
+ * smla_bwd_phased's at that phase: dq and d_sink as smla_bwd's bit for bit,
+ * dkv up to the fp32 summation order across phases.
+ * Errors: as smla_bwd; SMLA_ERR_WORKSPACE (before anything is enqueued) when
+ * even a one-token phase does not fit the array (its fixed part is about
+ * 4*T*H + 2 KiB*num_kv bytes); SMLA_ERR_HIP if the array's device address
+ * cannot be obtained.
+ * Every call on one GPU uses that GPU's one array, and nothing in it needs to
+ * be cleared between calls (every cell is written before it is read).  Calls
+ * that may run at the same time on one GPU (on different streams) race on the
+ * array and give wrong results: order them on one stream.
+ */
+int smla_bwd_noalloc(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+                     const float* lse, const int32_t* idx, const float* sink, const float* dlse,
+                     int T, int H, int num_kv, int topk, float scale, uint32_t flags,
+                     uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* The backward's stages, exported individually (same conventions)          */
 /* ------------------------------------------------------------------------ */

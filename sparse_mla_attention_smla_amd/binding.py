@@ -6,7 +6,8 @@ in the library's HIP kernels; there is no fallback path.  If the library is
 missing, every call raises.
 
 Function names follow the C entry points: smla_fwd, smla_bwd, smla_bwd_phased,
-smla_delta, smla_dq, smla_interm, smla_build_csr, smla_gather, smla_dsink.
+smla_bwd_noalloc, smla_delta, smla_dq, smla_interm, smla_build_csr, smla_gather,
+smla_dsink.
 """
 from __future__ import annotations
 
@@ -41,6 +42,7 @@ _SIGNATURES = {
     "smla_bwd_phased_workspace_bytes": ([_I, _I, _I, _I, _I, _U], _Z),
     "smla_bwd_phased": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _I, _P, _P, _P, _P, _P,
                          _Z, _P], _I),
+    "smla_bwd_noalloc": ([_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P, _P, _P, _P], _I),
     "smla_delta": ([_P, _P, _P, _I, _I, _P, _P], _I),
     "smla_dq": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "smla_interm": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
@@ -276,6 +278,22 @@ def smla_bwd_phased(q, kv, dO, o, lse, idx, sink=None, scale=None, phase_tokens=
         _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
         _default_scale(scale), 0, int(phase_tokens), _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv),
         _ptr(workspace), ws_bytes, _stream(q.device)))
+    if count_invalid:
+        return dq, dkv, d_sink, n_inv
+    return dq, dkv, d_sink
+
+
+def smla_bwd_noalloc(q, kv, dO, o, lse, idx, sink=None, scale=None, out=None, count_invalid=False,
+                     dlse=None):
+    """The backward on the library's fixed device scratch (no workspace, no
+    allocation inside the call).  With `out` (and count_invalid False) this
+    function allocates nothing either.  Returns (dq, dkv, d_sink[, n_invalid])."""
+    T, H, N, K = _check_bwd_inputs(q, kv, dO, o, lse, idx, sink, dlse)
+    dq, dkv, d_sink = _bwd_outputs(q, kv, H, sink, out)
+    n_inv = torch.empty((1,), dtype=torch.int32, device=q.device) if count_invalid else None
+    _check("smla_bwd_noalloc", lib().smla_bwd_noalloc(
+        _ptr(q), _ptr(kv), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink), _ptr(dlse), T, H, N, K,
+        _default_scale(scale), 0, _ptr(dq), _ptr(dkv), _ptr(d_sink), _ptr(n_inv), _stream(q.device)))
     if count_invalid:
         return dq, dkv, d_sink, n_inv
     return dq, dkv, d_sink

@@ -394,11 +394,67 @@ int smla_bwd_timed(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, co
                     d_sink, n_invalid, workspace, workspace_bytes, stream, events);
 }
 
-int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
-                    const float* lse, const int32_t* idx, const float* sink, const float* dlse,
-                    int T, int H, int num_kv, int topk, float scale, uint32_t flags, int phase_tokens,
-                    uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- scratch of the no-allocation backward ---------------------------------
+// A fixed device array holds the workspace of smla_bwd_noalloc.  Host code
+// never uses the array's name as a device address: once per device, with that
+// device current, hipGetSymbolAddress yields the device's own copy, and that
+// pointer is what the kernels receive.
+constexpr size_t kScratchBytes = (size_t)256 << 20;
+void* g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+smla_status scratch_of_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return SMLA_ERR_ARCH;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return SMLA_ERR_HIP;
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return SMLA_OK;
+}
+
+// Largest token phase whose phased workspace fits the scratch (0 if even one
+// token does not).
+int noalloc_phase_tokens(int T, int H, int num_kv, int topk) {
+    auto fits = [&](int tp) { return phased_layout(T, H, num_kv, topk, tp).total <= kScratchBytes; };
+    if (!fits(1)) return 0;
+    int lo = 1, hi = T > 1 ? T : 1;
+    while (lo < hi) {
+        const int mid = lo + (hi - lo + 1) / 2;
+        if (fits(mid)) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+// The token-phased backward.  With use_helper false, every stage stays on the
+// caller's stream (no library-owned stream or event is created or used).  With
+// use_scratch, `workspace` is ignored and the phase must fit the scratch; its
+// address is taken only after every argument check has passed.
+int phased_impl(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+                const float* lse, const int32_t* idx, const float* sink, const float* dlse, int T,
+                int H, int num_kv, int topk, float scale, uint32_t flags, int phase_tokens,
+                uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* workspace,
+                size_t workspace_bytes, void* stream, bool use_helper, bool use_scratch = false) {
+    if (use_scratch) {
+        workspace = nullptr;
+        workspace_bytes = kScratchBytes;
+    }
     smla_status st = check_shape(T, H, num_kv, topk);
     if (st != SMLA_OK) return st;
     if (phase_tokens < 1) return SMLA_ERR_SHAPE;
@@ -412,7 +468,7 @@ int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, c
         !aligned(n_invalid, 4) || !aligned(workspace, 16))
         return SMLA_ERR_ALIGN;
     const PhasedLayout L = phased_layout(T, H, num_kv, topk, phase_tokens);
-    if (workspace == nullptr || workspace_bytes < L.total) return SMLA_ERR_WORKSPACE;
+    if ((!use_scratch && workspace == nullptr) || workspace_bytes < L.total) return SMLA_ERR_WORKSPACE;
     const size_t qb = (size_t)T * H * kD * 2;
     const size_t hb = (size_t)H * 4;
     const Range all[] = {{q, qb},
@@ -430,6 +486,7 @@ int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, c
                          {workspace, L.total}};
     if (!outputs_disjoint(all, 13, 8)) return SMLA_ERR_INVALID_ARG;
     if ((st = check_arch()) != SMLA_OK) return st;
+    if (use_scratch && (st = scratch_of_current_device(&workspace)) != SMLA_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
@@ -453,9 +510,12 @@ int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, c
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
     std::lock_guard<std::mutex> lk(g_side_mu);
-    bool cap_err = false;
-    SideStream* side = side_for(s, dev, &cap_err);
-    if (cap_err) return SMLA_ERR_HIP;
+    SideStream* side = nullptr;
+    if (use_helper) {
+        bool cap_err = false;
+        side = side_for(s, dev, &cap_err);
+        if (cap_err) return SMLA_ERR_HIP;
+    }
     hipStream_t aux = side != nullptr ? side->s : s;
     auto rec_wait = [&](hipEvent_t e, hipStream_t from, hipStream_t to) {
         return side == nullptr ||
@@ -496,6 +556,31 @@ int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, c
     if (n_invalid != nullptr && launch_sum_counts(inv, L.nphase, n_invalid, s) != hipSuccess)
         return SMLA_ERR_HIP;
     return SMLA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int smla_bwd_phased(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+                    const float* lse, const int32_t* idx, const float* sink, const float* dlse,
+                    int T, int H, int num_kv, int topk, float scale, uint32_t flags, int phase_tokens,
+                    uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    return phased_impl(q, kv, dO, o, lse, idx, sink, dlse, T, H, num_kv, topk, scale, flags,
+                       phase_tokens, dq, dkv, d_sink, n_invalid, workspace, workspace_bytes, stream,
+                       true);
+}
+
+int smla_bwd_noalloc(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const uint16_t* o,
+                     const float* lse, const int32_t* idx, const float* sink, const float* dlse,
+                     int T, int H, int num_kv, int topk, float scale, uint32_t flags,
+                     uint16_t* dq, uint16_t* dkv, float* d_sink, int32_t* n_invalid, void* stream) {
+    const smla_status st = check_shape(T, H, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    const int tp = noalloc_phase_tokens(T, H, num_kv, topk);
+    if (tp == 0) return SMLA_ERR_WORKSPACE;
+    return phased_impl(q, kv, dO, o, lse, idx, sink, dlse, T, H, num_kv, topk, scale, flags, tp, dq,
+                       dkv, d_sink, n_invalid, nullptr, 0, stream, false, true);
 }
 
 int smla_delta(const uint16_t* o, const uint16_t* dO, const float* dlse, int T, int H,
