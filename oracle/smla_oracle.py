@@ -30,7 +30,16 @@ design notes):
     replacing delta by delta - dlse gives.  Without it, dlse = 0;
   * d_sink[h] = -sum_t P_sink[t,h] * (delta[t,h] - dlse[t,h])
     (dO/dsink = -P_sink * O, dlse/dsink = P_sink);
-  * the CSR lists valid slots s = t*topk + k ordered by (index, s).
+  * the CSR lists valid slots s = t*topk + k ordered by (index, s);
+  * the has_pe=True variant, which the Contract section names (as the
+    forward's other path) without describing: q carries an extra positional
+    part q_pe [T,H,Dp] and the keys an extra part k_pe [N,Dp] shared by all
+    heads (DeepSeek's decoupled RoPE, Dp = 64), the logit is
+    scale * (<q, kv> + <q_pe, k_pe>), the values are kv alone.  Its extra
+    gradients are dq_pe = scale * sum_k dS k_pe and, per kv row,
+    dk_pe = sum over slots of sum_h scale * dS q_pe; everything else keeps its
+    has_pe=False form.  The scale is whatever the caller passes (the natural
+    choice is 1/sqrt(512 + Dp)).
 """
 from __future__ import annotations
 
@@ -121,17 +130,26 @@ def _sink_prob(sink: np.ndarray, lse: np.ndarray) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-def forward_token(q_t, kv64, idx_row, sink64, scale):
+def _logits(q_t, G, scale, qpe_t=None, Gpe=None):
+    """scale * (q kv^T [+ q_pe k_pe^T]) for the gathered rows G (and Gpe)."""
+    s = q_t @ G.T
+    if qpe_t is not None:
+        s = s + qpe_t @ Gpe.T
+    return scale * s
+
+
+def forward_token(q_t, kv64, idx_row, sink64, scale, qpe_t=None, kpe64=None):
     """One query token, all heads.  q_t: [H,D] float64.  Returns (O_t [H,D], lse_t [H]).
 
-    S_k = scale * <q, kv[idx_k]> over valid k; m = max(S, sink);
-    Z = sum_k exp(S_k - m) + exp(sink - m); lse = m + ln Z;
+    S_k = scale * <q, kv[idx_k]> (+ scale * <q_pe, k_pe[idx_k]>) over valid k;
+    m = max(S, sink); Z = sum_k exp(S_k - m) + exp(sink - m); lse = m + ln Z;
     O = sum_k exp(S_k - lse) kv[idx_k]   (the sink's value vector is zero).
     """
     H, Dh = q_t.shape
     v = _valid(idx_row, kv64.shape[0])
     G = kv64[idx_row[v]]                       # [nv, D]
-    s = scale * (q_t @ G.T)                    # [H, nv]
+    Gpe = None if kpe64 is None else kpe64[idx_row[v]]
+    s = _logits(q_t, G, scale, qpe_t, Gpe)     # [H, nv]
     m = np.maximum(s.max(axis=1) if G.shape[0] else np.full(H, -np.inf), sink64)
     lse = np.full(H, -np.inf)
     live = np.isfinite(m)
@@ -145,16 +163,19 @@ def forward_token(q_t, kv64, idx_row, sink64, scale):
     return O, lse
 
 
-def forward(q, kv, idx, sink, scale):
+def forward(q, kv, idx, sink, scale, q_pe=None, k_pe=None):
     """Sparse MLA forward in float64.  q [T,H,D], kv [N,D] (bf16 bits or floats),
-    idx [T,K] int, sink [H] or None.  Returns (O [T,H,D] f64, lse [T,H] f64)."""
+    idx [T,K] int, sink [H] or None; with has_pe also q_pe [T,H,Dp], k_pe [N,Dp].
+    Returns (O [T,H,D] f64, lse [T,H] f64)."""
     kv64 = _as64(kv)
+    kpe64 = None if k_pe is None else _as64(k_pe)
     T, H, Dh = np.shape(q)
     s64 = _sink64(sink, H)
     O = np.empty((T, H, Dh))
     lse = np.empty((T, H))
     for t in range(T):
-        O[t], lse[t] = forward_token(_as64(q[t]), kv64, np.asarray(idx[t]), s64, scale)
+        O[t], lse[t] = forward_token(_as64(q[t]), kv64, np.asarray(idx[t]), s64, scale,
+                                     None if q_pe is None else _as64(q_pe[t]), kpe64)
     return O, lse
 
 
@@ -169,26 +190,30 @@ def emit_forward_outputs(O, lse):
 # --------------------------------------------------------------------------
 
 
-def backward_token(q_t, kv64, dO_t, O_t, lse_t, idx_row, sink64, scale, dlse_t=None):
+def backward_token(q_t, kv64, dO_t, O_t, lse_t, idx_row, sink64, scale, dlse_t=None, qpe_t=None,
+                   kpe64=None):
     """Backward of one query token, all heads, following the phase definitions.
 
     delta = rowsum(O * dO)
-    P     = exp(S - lse)        S = scale * q kv^T        (0 on masked slots)
+    P     = exp(S - lse)        S = scale * q kv^T (+ scale * q_pe k_pe^T)   (0 on masked slots)
     dP    = dO kv^T
     dS    = P * (dP - delta + dlse)        (dlse = 0 when not given)
-    dq    = scale * dS kv
+    dq    = scale * dS kv                  dq_pe = scale * dS k_pe
     interm[k] = sum_h (scale * dS[h,k] q[h] + P[h,k] dO[h])   (0 on masked slots)
+    interm_pe[k] = sum_h scale * dS[h,k] q_pe[h]
     d_sink contribution = -P_sink * (delta - dlse)
 
-    Returns a dict of per-token arrays; P, dS are [H, K], interm is [K, D].
+    Returns a dict of per-token arrays; P, dS are [H, K], interm is [K, D]
+    (with has_pe also dq_pe [H, Dp] and interm_pe [K, Dp]).
     """
     H, Dh = q_t.shape
     K = idx_row.shape[0]
     v = _valid(idx_row, kv64.shape[0])
     G = kv64[idx_row[v]]
+    Gpe = None if kpe64 is None else kpe64[idx_row[v]]
     delta = np.sum(O_t * dO_t, axis=1)
     dl = np.zeros(H) if dlse_t is None else np.asarray(dlse_t, dtype=np.float64)
-    s = scale * (q_t @ G.T)
+    s = _logits(q_t, G, scale, qpe_t, Gpe)
     Pv = _probs(s, lse_t)
     dPv = dO_t @ G.T
     dSv = Pv * (dPv - delta[:, None] + dl[:, None])
@@ -200,18 +225,28 @@ def backward_token(q_t, kv64, dO_t, O_t, lse_t, idx_row, sink64, scale, dlse_t=N
     interm = np.zeros((K, Dh))
     interm[v] = scale * (dSv.T @ q_t) + Pv.T @ dO_t
     p_sink = _sink_prob(sink64, lse_t)
-    return {"dq": dq, "delta": delta, "P": P, "dS": dS, "interm": interm,
-            "dsink": -p_sink * (delta - dl), "valid": v}
+    out = {"dq": dq, "delta": delta, "P": P, "dS": dS, "interm": interm,
+           "dsink": -p_sink * (delta - dl), "valid": v}
+    if qpe_t is not None:
+        Dp = qpe_t.shape[1]
+        out["dq_pe"] = scale * (dSv @ Gpe) if G.shape[0] else np.zeros((H, Dp))
+        interm_pe = np.zeros((K, Dp))
+        interm_pe[v] = scale * (dSv.T @ qpe_t)
+        out["interm_pe"] = interm_pe
+    return out
 
 
-def backward(q, kv, dO, O, lse, idx, sink, scale, stages=False, dlse=None):
+def backward(q, kv, dO, O, lse, idx, sink, scale, stages=False, dlse=None, q_pe=None, k_pe=None):
     """Full backward in float64.  Inputs as consumed by the op: q, kv, dO, O as
-    bf16 bits (or floats), lse float, idx int, sink [H] or None, dlse [T,H] or None.
+    bf16 bits (or floats), lse float, idx int, sink [H] or None, dlse [T,H] or
+    None; with has_pe also q_pe [T,H,Dp] and k_pe [N,Dp].
 
     Returns dict with dq [T,H,D], dkv [N,D], d_sink [H] (None without a sink),
-    delta [T,H]; with stages=True also P, dS [T,H,K] and interm [T,K,D].
+    delta [T,H]; with has_pe also dq_pe [T,H,Dp] and dk_pe [N,Dp]; with
+    stages=True also P, dS [T,H,K] and interm [T,K,D] (and interm_pe).
     """
     kv64 = _as64(kv)
+    kpe64 = None if k_pe is None else _as64(k_pe)
     N, Dh = kv64.shape
     T, H, _ = np.shape(q)
     K = np.shape(idx)[1]
@@ -221,37 +256,58 @@ def backward(q, kv, dO, O, lse, idx, sink, scale, stages=False, dlse=None):
     dkv = np.zeros((N, Dh))
     delta = np.empty((T, H))
     dsink = np.zeros(H)
+    pe = kpe64 is not None
+    if pe:
+        Dp = kpe64.shape[1]
+        dq_pe = np.empty((T, H, Dp))
+        dk_pe = np.zeros((N, Dp))
     if stages:
         P = np.zeros((T, H, K))
         dS = np.zeros((T, H, K))
         interm = np.zeros((T, K, Dh))
+        if pe:
+            interm_pe = np.zeros((T, K, Dp))
     for t in range(T):
         row = np.asarray(idx[t])
         r = backward_token(_as64(q[t]), kv64, _as64(dO[t]), _as64(O[t]), lse64[t], row, s64, scale,
-                           None if dlse is None else dlse[t])
+                           None if dlse is None else dlse[t],
+                           _as64(q_pe[t]) if pe else None, kpe64)
         dq[t] = r["dq"]
         delta[t] = r["delta"]
         dsink += r["dsink"]
         v = r["valid"]
         np.add.at(dkv, row[v], r["interm"][v])
+        if pe:
+            dq_pe[t] = r["dq_pe"]
+            np.add.at(dk_pe, row[v], r["interm_pe"][v])
         if stages:
             P[t], dS[t], interm[t] = r["P"], r["dS"], r["interm"]
+            if pe:
+                interm_pe[t] = r["interm_pe"]
     out = {"dq": dq, "dkv": dkv, "d_sink": dsink if sink is not None else None, "delta": delta}
+    if pe:
+        out.update(dq_pe=dq_pe, dk_pe=dk_pe)
     if stages:
         out.update(P=P, dS=dS, interm=interm)
+        if pe:
+            out["interm_pe"] = interm_pe
     return out
 
 
-def backward_tokens(q, kv, dO, O, lse, idx, sink, scale, tokens, dlse=None):
-    """dq, delta, P, dS and interm for a subset of query tokens only."""
+def backward_tokens(q, kv, dO, O, lse, idx, sink, scale, tokens, dlse=None, q_pe=None, k_pe=None):
+    """dq, delta, P, dS and interm (with has_pe also dq_pe, interm_pe) for a
+    subset of query tokens only."""
     kv64 = _as64(kv)
+    kpe64 = None if k_pe is None else _as64(k_pe)
     H = np.shape(q)[1]
     s64 = _sink64(sink, H)
     lse64 = np.asarray(lse, dtype=np.float64)
     res = [backward_token(_as64(q[t]), kv64, _as64(dO[t]), _as64(O[t]), lse64[t],
-                          np.asarray(idx[t]), s64, scale, None if dlse is None else dlse[t])
+                          np.asarray(idx[t]), s64, scale, None if dlse is None else dlse[t],
+                          None if q_pe is None else _as64(q_pe[t]), kpe64)
            for t in tokens]
-    return {k: np.stack([r[k] for r in res]) for k in ("dq", "delta", "P", "dS", "interm")}
+    keys = ("dq", "delta", "P", "dS", "interm") + (("dq_pe", "interm_pe") if kpe64 is not None else ())
+    return {k: np.stack([r[k] for r in res]) for k in keys}
 
 
 def dkv_rows(q, kv, dO, O, lse, idx, sink, scale, rows, dlse=None):

@@ -30,6 +30,9 @@ Recipe (seed s = 1000 + workload.index):
 * dlse (an optional upstream gradient of lse, [T,H] float32) -- standard normal
   from ``np.random.default_rng([s, 4])``; its spread is that of delta for these
   inputs, so both terms of the shifted delta matter.
+* q_pe [T,H,64], k_pe [num_kv,64] (the positional parts of the has_pe=True
+  variant) -- standard normal rounded to bf16 like q and kv, tensors 5 and 6
+  of the same chunk-seeded scheme.
 """
 from __future__ import annotations
 
@@ -40,6 +43,7 @@ from dataclasses import dataclass
 import numpy as np
 
 D = 512  # fixed head dimension of the op
+DPE = 64  # width of the positional part of the has_pe=True variant
 
 
 @dataclass(frozen=True)
@@ -179,6 +183,14 @@ def make_dlse(name_or_workload) -> np.ndarray:
     """Seeded upstream gradient of lse for one workload: float32 [T, H]."""
     w = WORKLOADS[name_or_workload] if isinstance(name_or_workload, str) else name_or_workload
     return np.random.default_rng([1000 + w.index, 4]).standard_normal((w.T, w.H), dtype=np.float32)
+
+
+def make_pe(name_or_workload) -> tuple:
+    """Seeded positional parts for one workload: q_pe [T,H,64] and k_pe [num_kv,64]
+    as bf16 bits (uint16)."""
+    w = WORKLOADS[name_or_workload] if isinstance(name_or_workload, str) else name_or_workload
+    seed = 1000 + w.index
+    return normal_bf16((w.T, w.H, DPE), seed, 5), normal_bf16((w.num_kv, DPE), seed, 6)
 
 
 def shuffle_slots(idx: np.ndarray, seed: int) -> np.ndarray:

@@ -538,3 +538,118 @@ def test_generator_index_structure(name, nnz):
     if name == "skewed":
         counts = np.bincount(idx[valid], minlength=w.num_kv)
         assert counts[w.T] > 3000     # pool row 0 collects thousands of contributors
+
+
+# --------------------------------------------------------------------------
+# the has_pe=True variant: a positional part on q and on the keys only
+# --------------------------------------------------------------------------
+
+def _pe_parts(T, H, N, Dp, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((T, H, Dp)), rng.standard_normal((N, Dp))
+
+
+@pytest.mark.parametrize("with_sink", [True, False])
+def test_pe_backward_matches_central_differences(with_sink):
+    """L = <dO, O(q, q_pe, kv, k_pe, sink)>: every gradient, the two positional
+    ones included, against central differences (duplicate, -1, out-of-range and
+    all-masked slots as in the plain case)."""
+    D, Dp = 8, 4
+    q, kv, dO, idx, sink, scale = _fd_case(D, with_sink, seed=61 + with_sink)
+    q_pe, k_pe = _pe_parts(q.shape[0], q.shape[1], kv.shape[0], Dp, seed=62)
+    O, lse = orc.forward(q, kv, idx, sink, scale, q_pe=q_pe, k_pe=k_pe)
+    g = orc.backward(q, kv, dO, O, lse, idx, sink, scale, q_pe=q_pe, k_pe=k_pe)
+
+    def loss():
+        return float(np.sum(orc.forward(q, kv, idx, sink, scale, q_pe=q_pe, k_pe=k_pe)[0] * dO))
+
+    def fd(arr):
+        out = np.empty(arr.shape)
+        for i in np.ndindex(arr.shape):
+            x0 = arr[i]
+            eps = 1e-6 * max(1.0, abs(x0))
+            arr[i] = x0 + eps
+            lp = loss()
+            arr[i] = x0 - eps
+            lm = loss()
+            arr[i] = x0
+            out[i] = (lp - lm) / (2 * eps)
+        return out
+
+    for name, arr in (("dq", q), ("dq_pe", q_pe), ("dkv", kv), ("dk_pe", k_pe)):
+        np.testing.assert_allclose(g[name], fd(arr), rtol=1e-6, atol=1e-8, err_msg=name)
+    if with_sink:
+        np.testing.assert_allclose(g["d_sink"], fd(sink), rtol=1e-6, atol=1e-8)
+    assert np.all(g["dq_pe"][3] == 0.0)           # the all-masked row
+    # the gather phase on the positional intermediate gives dk_pe
+    st = orc.backward(q, kv, dO, O, lse, idx, sink, scale, stages=True, q_pe=q_pe, k_pe=k_pe)
+    np.testing.assert_allclose(orc.dkv_from_interm(st["interm_pe"], idx, kv.shape[0]), g["dk_pe"],
+                               rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("with_sink", [True, False])
+def test_pe_dense_causal_case_matches_torch_sdpa(with_sink):
+    """Dense causal case: SDPA with 576-wide queries/keys ([q, q_pe], [kv, k_pe]) and
+    512-wide values (kv) -- torch's attention allows the value width to differ."""
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    rng = np.random.default_rng(13)
+    T, H, D, Dp = 10, 3, 24, 8
+    scale = 1 / math.sqrt(D + Dp)
+    idx = np.full((T, T), -1, dtype=np.int64)
+    for t in range(T):
+        idx[t, : t + 1] = np.arange(t + 1)
+    q, kv, dO = rng.standard_normal((T, H, D)), rng.standard_normal((T, D)), rng.standard_normal((T, H, D))
+    q_pe, k_pe = rng.standard_normal((T, H, Dp)), rng.standard_normal((T, Dp))
+    sink = rng.standard_normal(H)
+    sk = sink if with_sink else None
+    O, lse = orc.forward(q, kv, idx, sk, scale, q_pe=q_pe, k_pe=k_pe)
+    g = orc.backward(q, kv, dO, O, lse, idx, sk, scale, q_pe=q_pe, k_pe=k_pe)
+
+    tq, tqp = torch.tensor(q, requires_grad=True), torch.tensor(q_pe, requires_grad=True)
+    tkv, tkp = torch.tensor(kv, requires_grad=True), torch.tensor(k_pe, requires_grad=True)
+    tsink = torch.tensor(sink, requires_grad=True)
+    z = lambda w: torch.zeros(1, w, dtype=torch.float64)
+    keys = torch.cat([torch.cat([tkv, tkp], 1), z(D + Dp)], 0)          # + the sink's key (logit via mask)
+    vals = torch.cat([tkv, z(D)], 0)                                     # the sink carries no value
+    mask = torch.full((H, T, T + 1), float("-inf"), dtype=torch.float64)
+    mask[:, :, :T] = torch.triu(torch.full((T, T), float("-inf"), dtype=torch.float64), 1)
+    if with_sink:
+        mask[:, :, T] = 0.0
+        mask = mask + torch.nn.functional.pad(tsink[:, None, None].expand(H, T, 1), (T, 0))
+    qh = torch.cat([tq, tqp], 2).permute(1, 0, 2)[None]
+    kh = keys[None, None].expand(1, H, T + 1, D + Dp)
+    vh = vals[None, None].expand(1, H, T + 1, D)
+    with sdpa_kernel(SDPBackend.MATH):
+        out = torch.nn.functional.scaled_dot_product_attention(qh, kh, vh, attn_mask=mask[None], scale=scale)
+    ref_O = out[0].permute(1, 0, 2)
+    np.testing.assert_allclose(O, ref_O.detach().numpy(), rtol=1e-12, atol=1e-13)
+    torch.sum(ref_O * torch.tensor(dO)).backward()
+    for name, t_ in (("dq", tq), ("dq_pe", tqp), ("dkv", tkv), ("dk_pe", tkp)):
+        np.testing.assert_allclose(g[name], t_.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+    if with_sink:
+        np.testing.assert_allclose(g["d_sink"], tsink.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_pe_zero_parts_reduce_to_the_plain_op():
+    """q_pe = 0 leaves every logit unchanged: O, lse, dq, dkv, d_sink equal the plain
+    op's and dk_pe = 0 exactly; k_pe = 0 likewise, with dq_pe = 0 exactly."""
+    q, kv, dO, idx, sink, scale = _random_case(21)
+    T, H, _ = q.shape
+    N = kv.shape[0]
+    q_pe, k_pe = _pe_parts(T, H, N, 6, seed=22)
+    O, lse = orc.forward(q, kv, idx, sink, scale)
+    g = orc.backward(q, kv, dO, O, lse, idx, sink, scale)
+    for qp, kp, zero in ((np.zeros_like(q_pe), k_pe, "dk_pe"), (q_pe, np.zeros_like(k_pe), "dq_pe")):
+        O2, lse2 = orc.forward(q, kv, idx, sink, scale, q_pe=qp, k_pe=kp)
+        np.testing.assert_array_equal(O2, O)
+        np.testing.assert_array_equal(lse2, lse)
+        g2 = orc.backward(q, kv, dO, O, lse, idx, sink, scale, q_pe=qp, k_pe=kp)
+        for k in ("dq", "dkv", "d_sink"):
+            np.testing.assert_allclose(g2[k], g[k], rtol=1e-13, atol=1e-15, err_msg=k)
+        assert np.all(g2[zero] == 0.0)
+    # a positional part that matches the content part doubles the logits: same as q scaled by 2
+    q_pe2, k_pe2 = q.copy(), kv.copy()
+    O3, lse3 = orc.forward(q, kv, idx, sink, scale, q_pe=q_pe2, k_pe=k_pe2)
+    O4, lse4 = orc.forward(2 * q, kv, idx, sink, scale)
+    np.testing.assert_allclose(O3, O4, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse3, lse4, rtol=1e-13)
