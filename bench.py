@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--stage-events", choices=["on", "off"], default="on",
                     help="time delta/dQ/intermediate/gather with events recorded inside the "
                          "timed calls (off: plain calls, stages timed through their entry points)")
+    ap.add_argument("--pe", choices=["on", "off"], default="on",
+                    help="also time the has_pe=True variant (smla_fwd_pe, smla_bwd_pe) on the same "
+                         "workload with seeded positional parts q_pe [T,H,64], k_pe [num_kv,64]")
     ap.add_argument("--mode", choices=["full", "profile"], default="full",
                     help="profile: only the timed backward calls, then a plain device copy of "
                          "COPY_BYTES (the reference for scaling HBM byte counters); prints no JSON")
@@ -177,6 +180,54 @@ def time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq, dk
             "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 1),
             "workspace_gib": round(ph_ws.numel() / 2 ** 30, 3),
             "full_workspace_gib": round(ws.numel() / 2 ** 30, 3)}
+
+
+def time_pe(B, w, q, kv, dO, idx, sink, reps):
+    """The has_pe=True variant on the same workload: ms per smla_bwd_pe call and per
+    smla_fwd_pe call, with seeded positional parts (scale 1/sqrt(512 + 64))."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_smla_amd import inputs
+    T, H, N, K = w.T, w.H, w.num_kv, w.topk
+    qpe_h, kpe_h = inputs.make_pe(w.name)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    q_pe, k_pe = d16(qpe_h), d16(kpe_h)
+    scale = 1.0 / math.sqrt(D + 64)
+    O, lse = B.smla_fwd_pe(q, q_pe, kv, k_pe, idx, sink, scale)
+    outs = (torch.empty_like(q), torch.empty_like(q_pe), torch.empty_like(kv), torch.empty_like(k_pe),
+            torch.empty(H, dtype=torch.float32, device="cuda"))
+    ws = torch.empty(B.bwd_pe_workspace_bytes(T, H, N, K), dtype=torch.uint8, device="cuda")
+
+    def bwd():
+        B.smla_bwd_pe(q, q_pe, kv, k_pe, dO, O, lse, idx, sink, scale, workspace=ws, out=outs)
+
+    def fwd():
+        B.smla_fwd_pe(q, q_pe, kv, k_pe, idx, sink, scale, out=(O, lse))
+
+    res = {}
+    for name, fn in (("bwd", bwd), ("fwd", fwd)):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        res[name] = a.elapsed_time(b) / reps
+    # nominal flops: the plain op's plus the positional products (S, dq_pe and the
+    # positional intermediate in the backward; S in the forward), 64 wide
+    bwd_flops = w.flops() + 6.0 * T * H * K * 64
+    fwd_flops = 4.0 * T * H * K * D + 2.0 * T * H * K * 64
+    del ws
+    return {"bwd_ms": round(res["bwd"], 4), "bwd_tflops": round(bwd_flops / (res["bwd"] * 1e-3) / 1e12, 1),
+            "bwd_frac_of_bf16_peak": round(bwd_flops / (res["bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "fwd_ms": round(res["fwd"], 4), "fwd_tflops": round(fwd_flops / (res["fwd"] * 1e-3) / 1e12, 1),
+            "note": "smla_bwd_pe / smla_fwd_pe with q_pe [T,H,64], k_pe [num_kv,64]; nominal flops "
+                    "10*T*H*topk*512 + 6*T*H*topk*64 (backward), 4*T*H*topk*512 + 2*T*H*topk*64 (forward)"}
 
 
 def cpu_baseline(w, n_tokens):
@@ -399,6 +450,11 @@ def main():
         phased_row = time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq2, dkv2,
                                  ds2, args.stage_steps)
 
+    pe_row = None
+    if args.pe == "on":
+        print("[bench] has_pe variant", file=sys.stderr, flush=True)
+        pe_row = time_pe(B, w, q, kv, dO, idx, sink, args.stage_steps)
+
     cpu = None
     if args.cpu_baseline == "on":
         print(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr,
@@ -434,6 +490,7 @@ def main():
                          "entry points alone" if args.stage_events == "on" else "entry points alone"),
         "forward": forward,
         "phased": phased_row,
+        "has_pe": pe_row,
         "graph_replay": graph_row,
         "roofline": roofline,
         "cpu_baseline": cpu,

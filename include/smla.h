@@ -291,6 +291,49 @@ size_t smla_dsink_workspace_bytes(int T, int H);
 int smla_dsink(const float* lse, const float* delta, const float* sink, int T, int H,
                float* d_sink, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* The has_pe=True variant                                                   */
+/* ------------------------------------------------------------------------ */
+/*
+ * Page: aiter PR 4766, Contract section -- the backward is "the forward's
+ * has_pe=False path"; has_pe=True is the forward's other path, which the page
+ * names without describing.  Reading used here (DeepSeek's decoupled RoPE):
+ * the queries carry an extra positional part q_pe [T, H, 64] and the keys an
+ * extra head-shared part k_pe [num_kv, 64]; the logit of slot k is
+ * scale * (<q, kv_k> + <q_pe, k_pe_k>); the values are kv alone (512 wide),
+ * so O, lse, delta and dkv keep their has_pe=False definitions, and the extra
+ * gradients are dq_pe = scale * sum_k dS k_pe_k and, per kv row j,
+ * dk_pe[j] = sum over the slots (t, k) with idx = j of sum_h scale*dS q_pe[t,h].
+ * The scale is the caller's (1/sqrt(512 + 64) is the natural choice).
+ * All conventions (masking, sink, alignment, overlap, streams, determinism)
+ * are those of smla_fwd / smla_bwd; q_pe, k_pe, dq_pe, dk_pe are bf16 and
+ * need 16-byte alignment.
+ */
+#define SMLA_DPE 64
+
+/* smla_fwd with the positional part: o bf16 [T,H,512], lse float [T,H] (sink-inclusive). */
+int smla_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                const int32_t* idx, const float* sink, int T, int H, int num_kv, int topk, float scale,
+                uint16_t* o, float* lse, void* stream);
+
+/* Bytes of workspace smla_bwd_pe needs (0 on a shape error or flags != 0). */
+size_t smla_bwd_pe_workspace_bytes(int T, int H, int num_kv, int topk, uint32_t flags);
+
+/*
+ * smla_bwd_pe -- smla_bwd with the positional part: additionally reads q_pe
+ * [T,H,64] and k_pe [num_kv,64] and writes dq_pe bf16 [T,H,64] and dk_pe bf16
+ * [num_kv,64] (rows no slot addresses get zeros).  The stages are smla_bwd's
+ * (the dS/P blocks now come from the logits with the positional term), plus a
+ * positional intermediate [T*topk, 64] contracted over the heads and its
+ * gather through the same inverted index.  flags must be 0.
+ */
+int smla_bwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                const uint16_t* dO, const uint16_t* o, const float* lse, const int32_t* idx,
+                const float* sink, const float* dlse, int T, int H, int num_kv, int topk, float scale,
+                uint32_t flags, uint16_t* dq, uint16_t* dq_pe, uint16_t* dkv, uint16_t* dk_pe,
+                float* d_sink, int32_t* n_invalid, void* workspace, size_t workspace_bytes,
+                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,7 +7,7 @@ missing, every call raises.
 
 Function names follow the C entry points: smla_fwd, smla_bwd, smla_bwd_phased,
 smla_bwd_noalloc, smla_delta, smla_dq, smla_interm, smla_build_csr, smla_gather,
-smla_dsink.
+smla_dsink, and the has_pe=True variant smla_fwd_pe, smla_bwd_pe.
 """
 from __future__ import annotations
 
@@ -20,6 +20,7 @@ import threading
 import torch
 
 D = 512
+DPE = 64   # positional part of the has_pe=True variant
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsmla.so")
 
@@ -53,6 +54,10 @@ _SIGNATURES = {
     "smla_dsp_bytes": ([_I, _I, _I], _Z),
     "smla_dsink_workspace_bytes": ([_I, _I], _Z),
     "smla_dsink": ([_P, _P, _P, _I, _I, _P, _P, _Z, _P], _I),
+    "smla_fwd_pe": ([_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "smla_bwd_pe_workspace_bytes": ([_I, _I, _I, _I, _U], _Z),
+    "smla_bwd_pe": ([_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _U, _P, _P, _P, _P, _P, _P,
+                     _P, _Z, _P], _I),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -423,3 +428,72 @@ def smla_dsink(lse, delta, sink, d_sink=None, workspace=None):
     _check("smla_dsink", lib().smla_dsink(_ptr(lse), _ptr(delta), _ptr(sink), T, H, _ptr(d_sink),
                                           _ptr(ws), ws_bytes, _stream(dv)))
     return d_sink
+
+
+# ---------------------------------------------------------------------------
+# the has_pe=True variant (positional parts q_pe [T,H,64], k_pe [num_kv,64])
+# ---------------------------------------------------------------------------
+
+def _default_scale_pe(scale):
+    return 1.0 / math.sqrt(D + DPE) if scale is None else float(scale)
+
+
+def smla_fwd_pe(q, q_pe, kv, k_pe, idx, sink=None, scale=None, out=None):
+    """Forward with the positional part: (o bf16 [T,H,512], lse fp32 [T,H])."""
+    T, H, _ = q.shape
+    N, K = kv.shape[0], idx.shape[1]
+    dv = q.device
+    _need(q, "q", torch.bfloat16, (T, H, D))
+    _need(q_pe, "q_pe", torch.bfloat16, (T, H, DPE), dv)
+    _need(kv, "kv", torch.bfloat16, (N, D), dv)
+    _need(k_pe, "k_pe", torch.bfloat16, (N, DPE), dv)
+    _need(idx, "idx", torch.int32, (T, K), dv)
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (H,), dv)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty((T, H), dtype=torch.float32, device=dv)
+    else:
+        o, lse = out
+        _need(o, "o", torch.bfloat16, (T, H, D), dv)
+        _need(lse, "lse", torch.float32, (T, H), dv)
+    _check("smla_fwd_pe", lib().smla_fwd_pe(_ptr(q), _ptr(q_pe), _ptr(kv), _ptr(k_pe), _ptr(idx), _ptr(sink),
+                                            T, H, N, K, _default_scale_pe(scale), _ptr(o), _ptr(lse),
+                                            _stream(dv)))
+    return o, lse
+
+
+def bwd_pe_workspace_bytes(T, H, num_kv, topk) -> int:
+    n = lib().smla_bwd_pe_workspace_bytes(T, H, num_kv, topk, 0)
+    if n == 0:
+        raise SmlaError("smla_bwd_pe_workspace_bytes", 2)
+    return n
+
+
+def smla_bwd_pe(q, q_pe, kv, k_pe, dO, o, lse, idx, sink=None, scale=None, workspace=None, out=None,
+                count_invalid=False, dlse=None):
+    """Backward with the positional part: returns (dq, dq_pe, dkv, dk_pe, d_sink[, n_invalid]).
+    out, if given, is a tuple (dq, dq_pe, dkv, dk_pe, d_sink) of preallocated outputs."""
+    T, H, N, K = _check_bwd_inputs(q, kv, dO, o, lse, idx, sink, dlse)
+    dv = q.device
+    _need(q_pe, "q_pe", torch.bfloat16, (T, H, DPE), dv)
+    _need(k_pe, "k_pe", torch.bfloat16, (N, DPE), dv)
+    if out is None:
+        dq, dkv, d_sink = _bwd_outputs(q, kv, H, sink, None)
+        dq_pe = torch.empty_like(q_pe)
+        dk_pe = torch.empty_like(k_pe)
+    else:
+        dq, dq_pe, dkv, dk_pe, d_sink = out
+        dq, dkv, d_sink = _bwd_outputs(q, kv, H, sink, (dq, dkv, d_sink))
+        _need(dq_pe, "dq_pe", torch.bfloat16, (T, H, DPE), dv)
+        _need(dk_pe, "dk_pe", torch.bfloat16, (N, DPE), dv)
+    if workspace is None:
+        workspace = torch.empty((bwd_pe_workspace_bytes(T, H, N, K),), dtype=torch.uint8, device=dv)
+    ws_bytes = _workspace(workspace, "workspace", dv)
+    n_inv = torch.empty((1,), dtype=torch.int32, device=dv) if count_invalid else None
+    _check("smla_bwd_pe", lib().smla_bwd_pe(
+        _ptr(q), _ptr(q_pe), _ptr(kv), _ptr(k_pe), _ptr(dO), _ptr(o), _ptr(lse), _ptr(idx), _ptr(sink),
+        _ptr(dlse), T, H, N, K, _default_scale_pe(scale), 0, _ptr(dq), _ptr(dq_pe), _ptr(dkv), _ptr(dk_pe),
+        _ptr(d_sink), _ptr(n_inv), _ptr(workspace), ws_bytes, _stream(dv)))
+    res = (dq, dq_pe, dkv, dk_pe, d_sink)
+    return res + (n_inv,) if count_invalid else res

@@ -31,15 +31,22 @@
 
 namespace smla {
 
-template <int NW>
+// PE adds the has_pe=True variant's positional part: q_pe [T,H,64] (B operands
+// of two more S^T steps), k_pe [N,64] (a second, 4 KiB tile ring, see
+// kv_tile.hpp), and dq_pe [T,H,64] = scale * sum_k dS k_pe, accumulated from
+// the same dS fragment as dq.
+template <int NW, bool PE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
 void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 const uint16_t* __restrict__ dO, const float* __restrict__ lse,
                 const float* __restrict__ delta, const int32_t* __restrict__ idx, int H,
-                int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
+                int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp,
+                const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe,
+                uint16_t* __restrict__ dq_pe) {
     static_assert(kNBuf == 4, "the vmcnt bounds below assume a 4-deep ring");
-    constexpr int R = kBK / NW;   // DMA copies per wave per tile
+    constexpr int R = kBK / NW + (PE ? 4 / NW : 0);   // buffer->LDS copies per wave per tile
     __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char pe_tiles[PE ? kNBuf * kPeTileBytes : 16];
     __shared__ SlotList L;
 
     const int nhg = H / (NW * 16);
@@ -59,19 +66,51 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         qf[ds] = *reinterpret_cast<const u32x4*>(q + qrow + 32 * ds + 8 * g);
         dof[ds] = *reinterpret_cast<const u32x4*>(dO + qrow + 32 * ds + 8 * g);
     }
+    u32x4 qpf[2];
+    const size_t prow = ((size_t)t * H + h) * kDP;
+    if constexpr (PE) {
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) qpf[s2] = *reinterpret_cast<const u32x4*>(q_pe + prow + 32 * s2 + 8 * g);
+    }
     const float lse_h = lse[(size_t)t * H + h];
     const float bias = (lse_h == -INFINITY) ? INFINITY : lse_h * kLog2e;
     const float c = scale * kLog2e;
     const float dl = delta[(size_t)t * H + h];
     const i32x4 rsrc = make_rsrc(kv, (uint32_t)N * (kD * 2));
+    const i32x4 rsrc_pe = make_rsrc(k_pe, PE ? (uint32_t)N * kPeRow : 0u);
     const uint32_t ring = lds_addr(tiles);
-    const int rb = rows_base(c16, g), cb = cols_base(c16, g);
+    const uint32_t pe_ring = lds_addr(pe_tiles);
+    const int rb = rows_base(c16, g), cb = cols_base(c16, g), pcb = pe_cols_base(c16, g);
     const int ntk = (K + kBK - 1) / kBK;
     uint16_t* dsp_tok = dsp + (size_t)t * ntk * (2 * H) * kBK;
 
-    f32x4 acc[32];
+    f32x4 acc[32], acc_pe[4];
 #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc_pe[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto issue = [&](int ct) {
+        issue_tile<NW>(rsrc, &L, ct, ring + (ct % kNBuf) * kTileBytes, w, lane);
+        if constexpr (PE) issue_pe_tile<NW>(rsrc_pe, &L, ct, pe_ring + (ct % kNBuf) * kPeTileBytes, w, lane);
+    };
+    // the positional part of S^T for tile slot `slot` of the ring
+    auto s_pe = [&](f32x4 (&sacc)[2], int slot) {
+        if constexpr (PE) {
+            const char* pbuf = pe_tiles + slot * kPeTileBytes;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) sacc[st] = mfma16(pe_rows_a(pbuf, c16, g, st, s2), qpf[s2], sacc[st]);
+        }
+    };
+    auto dq_pe_step = [&](int slot, u32x4 bf) {
+        if constexpr (PE) {
+            const char* pbuf = pe_tiles + slot * kPeTileBytes;
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) acc_pe[dt] = mfma16(pe_cols_a(pbuf, pcb, dt), bf, acc_pe[dt]);
+        }
+    };
 
     // Software pipeline over the compacted tiles of a chunk.  Iteration j
     // turns tile j's S/dP accumulators into P and dS (VALU, stores), then runs
@@ -87,7 +126,7 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         const int n = L.n;
         const int ntile = (n + kBK - 1) / kBK;
 #pragma unroll
-        for (int p = 0; p < kNBuf - 1; ++p) issue_tile<NW>(rsrc, &L, p, ring + p * kTileBytes, w, lane);
+        for (int p = 0; p < kNBuf - 1; ++p) issue(p);
         if (ntile > 0) {
             f32x4 sacc[2], pacc[2];
             wait_vmcnt<(2 * R < 63 ? 2 * R : 63)>();
@@ -106,6 +145,7 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                     pacc[st] = mfma16(a, dof[ds], pacc[st]);
                 }
             }
+            s_pe(sacc, 0);
             // P and scale*dS of tile j from its accumulators; stores; B operand of dq
             auto softmax_grad = [&](int j) -> u32x4 {
                 float dss[2][4], ps[2][4];
@@ -136,7 +176,7 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                 // let the wait pass early.  Over-waiting on them is safe.
                 wait_vmcnt<(R < 63 ? R : 63)>();
                 __syncthreads();  // tile j+1 landed everywhere; ring slot of tile j-1 is free
-                issue_tile<NW>(rsrc, &L, j + kNBuf - 1, ring + ((j + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
+                issue(j + kNBuf - 1);
                 const u32x4 bf = softmax_grad(j);
                 const char* bufa = tiles + (j % kNBuf) * kTileBytes;
                 const char* bufb = tiles + ((j + 1) % kNBuf) * kTileBytes;
@@ -156,12 +196,15 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                         pacc[st] = mfma16(a, dof[ds], pacc[st]);
                     }
                 }
+                dq_pe_step(j % kNBuf, bf);
+                s_pe(sacc, (j + 1) % kNBuf);
             }
             const int jl = ntile - 1;
             const u32x4 bf = softmax_grad(jl);
             const char* bufl = tiles + (jl % kNBuf) * kTileBytes;
 #pragma unroll
             for (int dt = 0; dt < 32; ++dt) acc[dt] = mfma16(tile_cols_a(bufl, cb, dt), bf, acc[dt]);
+            dq_pe_step(jl % kNBuf, bf);
         }
         ctg += ntile;
         wait_vmcnt<0>();   // the ring's trailing copies land before LDS is reused
@@ -173,6 +216,13 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     for (int dt = 0; dt < 32; ++dt) {
         const u32x2 v = {pack_bf16(acc[dt][0], acc[dt][1]), pack_bf16(acc[dt][2], acc[dt][3])};
         *reinterpret_cast<u32x2*>(dq + qrow + 16 * dt + 4 * g) = v;
+    }
+    if constexpr (PE) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const u32x2 v = {pack_bf16(acc_pe[dt][0], acc_pe[dt][1]), pack_bf16(acc_pe[dt][2], acc_pe[dt][3])};
+            *reinterpret_cast<u32x2*>(dq_pe + prow + 16 * dt + 4 * g) = v;
+        }
     }
 }
 
@@ -781,8 +831,36 @@ hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, 
         return hipGetLastError();
     }
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
-    if (nw == 2) smla_k2_dq<2><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp);
-    else smla_k2_dq<1><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp);
+    if (nw == 2)
+        smla_k2_dq<2, false><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
+                                                    nullptr, nullptr, nullptr);
+    else
+        smla_k2_dq<1, false><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
+                                                   nullptr, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_dq_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                        const uint16_t* dO, const float* lse, const float* delta, const int32_t* idx, int T,
+                        int H, int N, int K, float scale, uint16_t* dq, uint16_t* dq_pe, uint16_t* dsp,
+                        hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int nw = dq_waves(H);
+    const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
+    switch (nw) {
+        case 4:
+            smla_k2_dq<4, true><<<blocks, 256, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
+                                                       q_pe, k_pe, dq_pe);
+            break;
+        case 2:
+            smla_k2_dq<2, true><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
+                                                       q_pe, k_pe, dq_pe);
+            break;
+        default:
+            smla_k2_dq<1, true><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
+                                                      q_pe, k_pe, dq_pe);
+            break;
+    }
     return hipGetLastError();
 }
 

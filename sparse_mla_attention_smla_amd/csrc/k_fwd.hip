@@ -17,13 +17,18 @@
 
 namespace smla {
 
-template <int NW>
+// PE adds the has_pe=True variant's positional part to the logits: q_pe
+// [T,H,64] as the B operand of two more S^T steps over a 4 KiB ring of k_pe
+// tiles (kv_tile.hpp); the values stay kv alone.
+template <int NW, bool PE>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
 void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                  const int32_t* __restrict__ idx, const float* __restrict__ sink, int H,
-                 int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse) {
-    constexpr int R = kBK / NW;
+                 int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse,
+                 const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe) {
+    constexpr int R = kBK / NW + (PE ? 4 / NW : 0);   // buffer->LDS copies per wave per tile
     __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char pe_tiles[PE ? kNBuf * kPeTileBytes : 16];
     __shared__ SlotList L;
 
     const int nhg = H / (NW * 16);
@@ -37,14 +42,25 @@ void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
     const int32_t* idx_row = idx + (size_t)t * K;
     if (w == 0) compact_slots(idx_row, K, N, 0, &L, lane);
 
-    u32x4 qf[16];
+    u32x4 qf[16], qpf[2];
 #pragma unroll
     for (int ds = 0; ds < 16; ++ds)
         qf[ds] = *reinterpret_cast<const u32x4*>(q + qrow + 32 * ds + 8 * g);
+    if constexpr (PE) {
+        const size_t prow = ((size_t)t * H + h) * kDP;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) qpf[s2] = *reinterpret_cast<const u32x4*>(q_pe + prow + 32 * s2 + 8 * g);
+    }
     const float c = scale * kLog2e;
     const i32x4 rsrc = make_rsrc(kv, (uint32_t)N * (kD * 2));
+    const i32x4 rsrc_pe = make_rsrc(k_pe, PE ? (uint32_t)N * kPeRow : 0u);
     const uint32_t ring = lds_addr(tiles);
+    const uint32_t pe_ring = lds_addr(pe_tiles);
     const int rb = rows_base(c16, g), cb = cols_base(c16, g);
+    auto issue = [&](int ct) {
+        issue_tile<NW>(rsrc, &L, ct, ring + (ct % kNBuf) * kTileBytes, w, lane);
+        if constexpr (PE) issue_pe_tile<NW>(rsrc_pe, &L, ct, pe_ring + (ct % kNBuf) * kPeTileBytes, w, lane);
+    };
 
     f32x4 acc[32];
 #pragma unroll
@@ -58,12 +74,12 @@ void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
         const int n = L.n;
         const int ntile = (n + kBK - 1) / kBK;
 #pragma unroll
-        for (int p = 0; p < kNBuf - 1; ++p) issue_tile<NW>(rsrc, &L, p, ring + p * kTileBytes, w, lane);
+        for (int p = 0; p < kNBuf - 1; ++p) issue(p);
         for (int it = 0; it < ntile; ++it) {
             // copies issued after tile `it`: always the next two tiles (2R)
             wait_vmcnt<(2 * R < 63 ? 2 * R : 63)>();
             __syncthreads();
-            issue_tile<NW>(rsrc, &L, it + kNBuf - 1, ring + ((it + kNBuf - 1) % kNBuf) * kTileBytes, w, lane);
+            issue(it + kNBuf - 1);
             const char* buf = tiles + (it % kNBuf) * kTileBytes;
 
             // four accumulation chains: both 16-slot halves, even and odd d-steps
@@ -77,6 +93,14 @@ void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
                     sacc[st] = mfma16(tile_rows_a(buf, rb, st, ds), qf[ds], sacc[st]);
                     sodd[st] = mfma16(tile_rows_a(buf, rb, st, ds + 1), qf[ds + 1], sodd[st]);
                 }
+            if constexpr (PE) {
+                const char* pbuf = pe_tiles + (it % kNBuf) * kPeTileBytes;
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    sacc[st] = mfma16(pe_rows_a(pbuf, c16, g, st, 0), qpf[0], sacc[st]);
+                    sodd[st] = mfma16(pe_rows_a(pbuf, c16, g, st, 1), qpf[1], sodd[st]);
+                }
+            }
 #pragma unroll
             for (int st = 0; st < 2; ++st) sacc[st] += sodd[st];
             float x[2][4];
@@ -149,9 +173,23 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
     const int nw = dq_waves(H);
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
     switch (nw) {
-        case 4: smla_k7_fwd<4><<<blocks, 256, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse); break;
-        case 2: smla_k7_fwd<2><<<blocks, 128, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse); break;
-        default: smla_k7_fwd<1><<<blocks, 64, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse); break;
+        case 4: smla_k7_fwd<4, false><<<blocks, 256, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse, nullptr, nullptr); break;
+        case 2: smla_k7_fwd<2, false><<<blocks, 128, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse, nullptr, nullptr); break;
+        default: smla_k7_fwd<1, false><<<blocks, 64, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse, nullptr, nullptr); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                         const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
+                         uint16_t* o, float* lse, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    const int nw = dq_waves(H);
+    const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
+    switch (nw) {
+        case 4: smla_k7_fwd<4, true><<<blocks, 256, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse, q_pe, k_pe); break;
+        case 2: smla_k7_fwd<2, true><<<blocks, 128, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse, q_pe, k_pe); break;
+        default: smla_k7_fwd<1, true><<<blocks, 64, 0, s>>>(q, kv, idx, sink, H, N, K, scale, o, lse, q_pe, k_pe); break;
     }
     return hipGetLastError();
 }

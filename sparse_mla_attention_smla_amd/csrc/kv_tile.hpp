@@ -188,4 +188,48 @@ __device__ __forceinline__ u32x4 tile_cols_a(const char* buf, int base, int dt) 
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// ---- positional key rows (the has_pe=True variant) ------------------------
+// A head-shared positional key part of kDP = 64 bf16 (128 bytes) per kv row.
+// A tile's 32 rows sit contiguously in LDS ([32][64], 4 KiB), written by four
+// 1 KiB buffer->LDS copies: copy c covers tile rows 8c..8c+7, lane l fetching
+// 16-byte chunk l%8 of row 8c + l/8 (so the LDS image is the rows back to
+// back).  Tail positions fetch from past the buffer's range and land as zeros.
+constexpr int kDP = 64;
+constexpr int kPeRow = kDP * 2;              // 128 bytes
+constexpr int kPeTileBytes = kBK * kPeRow;   // 4,096 bytes
+
+// Copies of positional tile `ct` issued by wave w of NW (NW in {1, 2, 4}):
+// copies w, w + NW, ... of the four, i.e. exactly 4/NW per wave.
+template <int NW>
+__device__ __forceinline__ void issue_pe_tile(i32x4 rsrc, const SlotList* L, int ct, uint32_t buf, int w,
+                                              int lane) {
+    static_assert(NW == 1 || NW == 2 || NW == 4, "four copies split evenly over the waves");
+    constexpr int kP = 4 / NW;
+    const int n = L->n;
+#pragma unroll
+    for (int i = 0; i < kP; ++i) {
+        const int c = w + NW * i;
+        const int pos = ct * kBK + 8 * c + (lane >> 3);
+        const int rowv = L->row[pos < kChunk ? pos : kChunk - 1];
+        const int row = pos < n ? rowv : kOobRow;
+        copy_row_to_lds(rsrc, buf + c * 1024, row * kPeRow + (lane & 7) * 16);
+    }
+}
+
+// S^T A operand of the positional part: lane (c16, g) reads tile row
+// 16*st + c16, positional elements 32*s + 8g .. +7 (s = 0, 1).
+__device__ __forceinline__ u32x4 pe_rows_a(const char* buf, int c16, int g, int st, int s) {
+    return *reinterpret_cast<const u32x4*>(buf + (16 * st + c16) * kPeRow + s * 64 + g * 16);
+}
+
+// Transposed A operand of dq_pe^T = kpe_tile^T . dS^T for positional d-tile dt
+// (dt = 0..3): the same lane pattern as tile_cols_a with the 128-byte pitch.
+__device__ __forceinline__ int pe_cols_base(int c16, int g) { return (4 * g + (c16 >> 2)) * kPeRow + (c16 & 3) * 8; }
+
+__device__ __forceinline__ u32x4 pe_cols_a(const char* buf, int base, int dt) {
+    const u32x2 lo = ds_read_tr16(buf + base + dt * 32);
+    const u32x2 hi = ds_read_tr16(buf + base + 16 * kPeRow + dt * 32);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 }  // namespace smla

@@ -13,6 +13,7 @@
 #include <mutex>
 
 #include "smla.h"
+#include "kv_tile.hpp"
 #include "smla_launch.hpp"
 #include "smla_device.hpp"
 
@@ -164,6 +165,26 @@ BwdLayout bwd_layout(int T, int H, int num_kv, int topk) {
     L.csr = take(csr_scratch_bytes(M, num_kv));
     L.gather = take(gather_scratch_bytes(M, num_kv));
     L.dsink = take((size_t)(dsink_blocks(T) > 0 ? dsink_blocks(T) : 1) * H * 4);
+    L.total = off;
+    return L;
+}
+
+// The has_pe=True backward: the plain layout plus the positional intermediate
+// [T*topk, 64] bf16 and the positional gather partials.
+struct PeLayout {
+    BwdLayout base;
+    size_t interm_pe, gather_pe, total;
+};
+
+PeLayout pe_layout(int T, int H, int num_kv, int topk) {
+    PeLayout L;
+    L.base = bwd_layout(T, H, num_kv, topk);
+    const int64_t M = (int64_t)T * topk;
+    size_t off = L.base.total;
+    L.interm_pe = off;
+    off += align_up((size_t)M * kDP * 2, kWsAlign);
+    L.gather_pe = off;
+    off += gather_pe_scratch_bytes(M, num_kv);
     L.total = off;
     return L;
 }
@@ -708,6 +729,133 @@ int smla_dsink(const float* lse, const float* delta, const float* sink, int T, i
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_dsink(lse, delta, sink, T, H, static_cast<float*>(workspace), d_sink,
                                    static_cast<hipStream_t>(stream)));
+}
+
+// ---- the has_pe=True variant -------------------------------------------------
+
+size_t smla_bwd_pe_workspace_bytes(int T, int H, int num_kv, int topk, uint32_t flags) {
+    if (flags != 0 || check_shape(T, H, num_kv, topk) != SMLA_OK) return 0;
+    return pe_layout(T, H, num_kv, topk).total;
+}
+
+int smla_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                const int32_t* idx, const float* sink, int T, int H, int num_kv, int topk, float scale,
+                uint16_t* o, float* lse, void* stream) {
+    smla_status st = check_shape(T, H, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    if (!std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !q_pe || !idx || !o || !lse)) return SMLA_ERR_INVALID_ARG;
+    if (!kv || !k_pe) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(q_pe, 16) || !aligned(kv, 16) || !aligned(k_pe, 16) ||
+        !aligned(o, 16) || !aligned(idx, 4) || !aligned(lse, 4) || !aligned(sink, 4))
+        return SMLA_ERR_ALIGN;
+    const size_t qb = (size_t)T * H * kD * 2;
+    const Range all[] = {{q, qb},
+                         {q_pe, (size_t)T * H * kDP * 2},
+                         {kv, (size_t)num_kv * kD * 2},
+                         {k_pe, (size_t)num_kv * kDP * 2},
+                         {idx, (size_t)T * topk * 4},
+                         {sink, sink ? (size_t)H * 4 : 0},
+                         {o, qb},
+                         {lse, (size_t)T * H * 4}};
+    if (!outputs_disjoint(all, 8, 6)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+    return hip_status(launch_fwd_pe(q, q_pe, kv, k_pe, idx, sink, T, H, num_kv, topk, scale, o, lse,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+int smla_bwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                const uint16_t* dO, const uint16_t* o, const float* lse, const int32_t* idx,
+                const float* sink, const float* dlse, int T, int H, int num_kv, int topk, float scale,
+                uint32_t flags, uint16_t* dq, uint16_t* dq_pe, uint16_t* dkv, uint16_t* dk_pe,
+                float* d_sink, int32_t* n_invalid, void* workspace, size_t workspace_bytes,
+                void* stream) {
+    smla_status st = check_shape(T, H, num_kv, topk);
+    if (st != SMLA_OK) return st;
+    if (flags != 0 || !std::isfinite(scale)) return SMLA_ERR_INVALID_ARG;
+    if (!kv || !k_pe || !dkv || !dk_pe) return SMLA_ERR_INVALID_ARG;
+    if (T > 0 && (!q || !q_pe || !dO || !o || !lse || !idx || !dq || !dq_pe)) return SMLA_ERR_INVALID_ARG;
+    if ((sink == nullptr) != (d_sink == nullptr)) return SMLA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(q_pe, 16) || !aligned(kv, 16) || !aligned(k_pe, 16) ||
+        !aligned(dO, 16) || !aligned(o, 16) || !aligned(dq, 16) || !aligned(dq_pe, 16) ||
+        !aligned(dkv, 16) || !aligned(dk_pe, 16) || !aligned(lse, 4) || !aligned(idx, 4) ||
+        !aligned(sink, 4) || !aligned(dlse, 4) || !aligned(d_sink, 4) || !aligned(n_invalid, 4) ||
+        !aligned(workspace, 16))
+        return SMLA_ERR_ALIGN;
+    const PeLayout L = pe_layout(T, H, num_kv, topk);
+    if (workspace == nullptr || workspace_bytes < L.total) return SMLA_ERR_WORKSPACE;
+    const size_t qb = (size_t)T * H * kD * 2, pb = (size_t)T * H * kDP * 2;
+    const size_t hb = (size_t)H * 4;
+    const Range all[] = {{q, qb},
+                         {q_pe, pb},
+                         {kv, (size_t)num_kv * kD * 2},
+                         {k_pe, (size_t)num_kv * kDP * 2},
+                         {dO, qb},
+                         {o, qb},
+                         {lse, (size_t)T * H * 4},
+                         {idx, (size_t)T * topk * 4},
+                         {sink, sink ? hb : 0},
+                         {dlse, dlse ? (size_t)T * H * 4 : 0},
+                         {dq, qb},
+                         {dq_pe, pb},
+                         {dkv, (size_t)num_kv * kD * 2},
+                         {dk_pe, (size_t)num_kv * kDP * 2},
+                         {d_sink, d_sink ? hb : 0},
+                         {n_invalid, n_invalid ? 4u : 0u},
+                         {workspace, L.total}};
+    if (!outputs_disjoint(all, 17, 10)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_arch()) != SMLA_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    const BwdLayout& B = L.base;
+    float* delta = reinterpret_cast<float*>(ws + B.delta);
+    uint16_t* dsp = reinterpret_cast<uint16_t*>(ws + B.dsp);
+    uint16_t* interm = reinterpret_cast<uint16_t*>(ws + B.interm);
+    uint16_t* interm_pe = reinterpret_cast<uint16_t*>(ws + L.interm_pe);
+    int32_t* row_ptr = reinterpret_cast<int32_t*>(ws + B.row_ptr);
+    int32_t* slots = reinterpret_cast<int32_t*>(ws + B.slots);
+    const int64_t M = (int64_t)T * topk;
+    const CsrScratch cs = csr_carve(ws + B.csr, M, num_kv);
+    const GatherScratch gs = gather_carve(ws + B.gather, M, num_kv);
+    float* dsink_part = reinterpret_cast<float*>(ws + B.dsink);
+    float* pe_partial = reinterpret_cast<float*>(ws + L.gather_pe);
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    bool cap_err = false;
+    SideStream* side = side_for(s, dev, &cap_err);
+    if (cap_err) return SMLA_ERR_HIP;
+    // the same stage order and helper-stream use as smla_bwd, plus the
+    // positional intermediate and its gather
+    hipStream_t aux = side != nullptr ? side->s : s;
+    if (side != nullptr) {
+        if (hipEventRecord(side->fork, s) != hipSuccess ||
+            hipStreamWaitEvent(aux, side->fork, 0) != hipSuccess)
+            return SMLA_ERR_HIP;
+    }
+    if (launch_csr(idx, M, num_kv, cs, row_ptr, slots, n_invalid, aux) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_gather_plan(row_ptr, M, num_kv, gs, aux) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_delta(o, dO, dlse, (int64_t)T * H, delta, s) != hipSuccess) return SMLA_ERR_HIP;
+    if (sink != nullptr) {
+        if (side != nullptr && (hipEventRecord(side->after_delta, s) != hipSuccess ||
+                                hipStreamWaitEvent(aux, side->after_delta, 0) != hipSuccess))
+            return SMLA_ERR_HIP;
+        if (launch_dsink(lse, delta, sink, T, H, dsink_part, d_sink, aux) != hipSuccess)
+            return SMLA_ERR_HIP;
+    }
+    if (side != nullptr && hipEventRecord(side->join, aux) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_dq_pe(q, q_pe, kv, k_pe, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dq_pe, dsp, s) !=
+        hipSuccess)
+        return SMLA_ERR_HIP;
+    if (launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm, s) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_interm_pe(q_pe, dsp, idx, T, H, num_kv, topk, interm_pe, s) != hipSuccess) return SMLA_ERR_HIP;
+    if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_gather_sum(interm, row_ptr, slots, M, num_kv, gs, dkv, s) != hipSuccess) return SMLA_ERR_HIP;
+    if (launch_gather_pe(interm_pe, row_ptr, slots, M, num_kv, gs, pe_partial, dk_pe, s) != hipSuccess)
+        return SMLA_ERR_HIP;
+    return SMLA_OK;
 }
 
 }  // extern "C"

@@ -72,6 +72,23 @@ hipError_t launch_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* 
                          const int32_t* idx, int T, int H, int N, int K, uint16_t* interm,
                          hipStream_t s);
 
+// ---- the has_pe=True variant (positional part of width 64) -----------------
+hipError_t launch_dq_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                        const uint16_t* dO, const float* lse, const float* delta, const int32_t* idx, int T,
+                        int H, int N, int K, float scale, uint16_t* dq, uint16_t* dq_pe, uint16_t* dsp,
+                        hipStream_t s);
+hipError_t launch_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                         const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
+                         uint16_t* o, float* lse, hipStream_t s);
+hipError_t launch_interm_pe(const uint16_t* q_pe, const uint16_t* dsp, const int32_t* idx, int T, int H,
+                            int N, int K, uint16_t* interm_pe, hipStream_t s);
+size_t gather_pe_scratch_bytes(int64_t M, int N);
+// sums of the positional intermediate per kv row, over the segments of an
+// existing gather plan (launch_gather_plan on the same row_ptr)
+hipError_t launch_gather_pe(const uint16_t* interm_pe, const int32_t* row_ptr, const int32_t* slots,
+                            int64_t M, int N, const GatherScratch& plan, float* partial, uint16_t* dk_pe,
+                            hipStream_t s);
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace smla

@@ -94,10 +94,17 @@ def oracle_backward_chunked(x, dlse=None, chunk=32, workers=None):
     dkv = np.zeros((N, Dh))
     dsink = np.zeros(H)
 
+    pe = x.get("q_pe") is not None
+    scale = x.get("scale", SCALE)
+    if pe:
+        dq_pe = np.empty((T, H, x["q_pe"].shape[2]))
+        dk_pe = np.zeros((N, x["k_pe"].shape[1]))
+
     def run(t0):
         t1 = min(T, t0 + chunk)
         r = orc.backward(x["q"][t0:t1], x["kv"], x["dO"][t0:t1], x["O"][t0:t1], x["lse"][t0:t1],
-                         x["idx"][t0:t1], x["sink"], SCALE, dlse=None if dlse is None else dlse[t0:t1])
+                         x["idx"][t0:t1], x["sink"], scale, dlse=None if dlse is None else dlse[t0:t1],
+                         q_pe=x["q_pe"][t0:t1] if pe else None, k_pe=x["k_pe"] if pe else None)
         return t0, t1, r
 
     starts = list(range(0, T, chunk))
@@ -109,7 +116,13 @@ def oracle_backward_chunked(x, dlse=None, chunk=32, workers=None):
                 dkv += r["dkv"]
                 if r["d_sink"] is not None:
                     dsink += r["d_sink"]
-    return {"dq": dq, "dkv": dkv, "d_sink": dsink if x["sink"] is not None else None, "delta": delta}
+                if pe:
+                    dq_pe[t0:t1] = r["dq_pe"]
+                    dk_pe += r["dk_pe"]
+    out = {"dq": dq, "dkv": dkv, "d_sink": dsink if x["sink"] is not None else None, "delta": delta}
+    if pe:
+        out.update(dq_pe=dq_pe, dk_pe=dk_pe)
+    return out
 
 
 def oracle_forward_chunked(x, chunk=32, workers=None):
@@ -126,9 +139,13 @@ def oracle_forward_chunked(x, chunk=32, workers=None):
     O = np.empty((T, H, Dh))
     lse = np.empty((T, H))
 
+    pe = x.get("q_pe") is not None
+
     def run(t0):
         t1 = min(T, t0 + chunk)
-        O[t0:t1], lse[t0:t1] = orc.forward(x["q"][t0:t1], x["kv"], x["idx"][t0:t1], x["sink"], SCALE)
+        O[t0:t1], lse[t0:t1] = orc.forward(x["q"][t0:t1], x["kv"], x["idx"][t0:t1], x["sink"],
+                                           x.get("scale", SCALE), q_pe=x["q_pe"][t0:t1] if pe else None,
+                                           k_pe=x["k_pe"] if pe else None)
 
     with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
         list(ex.map(run, range(0, T, chunk)))
@@ -152,6 +169,19 @@ def workload(name: str):
 @functools.lru_cache(maxsize=2)
 def workload_nosink(name: str):
     return _with_forward(inputs.make(name, sink=False))
+
+
+SCALE_PE = 1.0 / math.sqrt(512 + 64)   # the has_pe=True workloads' scale
+
+
+@functools.lru_cache(maxsize=2)
+def workload_pe(name: str, sink: bool = True):
+    """A seeded workload with the positional parts q_pe, k_pe (scale 1/sqrt(576)),
+    plus the oracle forward's rounded O and lse."""
+    x = dict(inputs.make(name, sink=sink))
+    x["q_pe"], x["k_pe"] = inputs.make_pe(name)
+    x["scale"] = SCALE_PE
+    return _with_forward(x)
 
 
 @functools.lru_cache(maxsize=2)

@@ -34,7 +34,7 @@ def lib():
 
 def test_header_and_binding_agree(lib):
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 21
     assert sorted(B.EXPORTED) == names
 
 
@@ -158,6 +158,34 @@ def test_stage_argument_errors(lib):
     assert lib.smla_dsink(A, 2 * A, None, 4, 16, 3 * A, 4 * A, 1024, None) == INVALID
     assert lib.smla_fwd(A, 2 * A, 3 * A, None, 4, 16, 8, 16, float("inf"), 4 * A, 5 * A, None) == INVALID
     assert lib.smla_fwd(A, 2 * A, 3 * A, None, 4, 16, 8, 16, 0.1, A, 5 * A, None) == INVALID
+
+
+def test_pe_argument_errors(lib):
+    T, H, N, K = 64, 16, 64, 16
+    p = dict(q=A, q_pe=12 * A, kv=2 * A, k_pe=13 * A, dO=3 * A, o=4 * A, lse=5 * A, idx=6 * A, sink=7 * A,
+             dlse=None, dq=8 * A, dq_pe=14 * A, dkv=9 * A, dk_pe=15 * A, d_sink=10 * A, n_inv=None,
+             work=11 * A)
+
+    def call(flags=0, ws=1 << 34, T=T, **kw):
+        a = dict(p)
+        a.update(kw)
+        return lib.smla_bwd_pe(a["q"], a["q_pe"], a["kv"], a["k_pe"], a["dO"], a["o"], a["lse"], a["idx"],
+                               a["sink"], a["dlse"], T, H, N, K, 0.05, flags, a["dq"], a["dq_pe"], a["dkv"],
+                               a["dk_pe"], a["d_sink"], a["n_inv"], a["work"], ws, None)
+    assert call(flags=1) == INVALID
+    assert call(q_pe=None) == INVALID
+    assert call(dk_pe=None) == INVALID
+    assert call(q_pe=12 * A + 8) == ALIGN
+    assert call(dq_pe=A) == INVALID                          # dq_pe aliases q
+    assert call(dk_pe=13 * A) == INVALID                     # dk_pe aliases k_pe
+    assert call(ws=1024) == WORKSPACE
+    assert call() in (HIP, ARCH)
+    n = lib.smla_bwd_pe_workspace_bytes(4096, 128, 5120, 512, 0)
+    assert n - lib.smla_bwd_workspace_bytes(4096, 128, 5120, 512, 0) >= 4096 * 512 * 128   # + interm_pe
+    assert lib.smla_bwd_pe_workspace_bytes(4096, 128, 5120, 512, 2) == 0
+    assert lib.smla_fwd_pe(A, 12 * A, 2 * A, 13 * A, 6 * A, None, T, H, N, K, 0.1, 12 * A, 5 * A, None) == INVALID
+    assert lib.smla_fwd_pe(A, None, 2 * A, 13 * A, 6 * A, None, T, H, N, K, 0.1, 4 * A, 5 * A, None) == INVALID
+    assert lib.smla_fwd_pe(A, 12 * A, 2 * A, 13 * A, 6 * A, None, T, H, N, K, 0.1, 4 * A, 5 * A, None) in (HIP, ARCH)
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

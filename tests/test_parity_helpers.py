@@ -71,3 +71,21 @@ def test_chunked_oracle_equals_one_plain_call():
         assert np.array_equal(got["delta"], ref["delta"])
         np.testing.assert_allclose(got["dkv"], ref["dkv"], rtol=1e-12, atol=1e-13)
         np.testing.assert_allclose(got["d_sink"], ref["d_sink"], rtol=1e-12)
+
+
+def test_chunked_oracle_with_positional_parts():
+    w = inputs.Workload("chkpe", 10, T=30, H=16, num_kv=40, topk=16, selection="swa_pool", window=6,
+                        pool_stride=2, pool_picks=10)
+    x = dict(inputs.make(w, sink=True))
+    x["q_pe"], x["k_pe"] = inputs.make_pe(w)
+    x["scale"] = hp.SCALE_PE
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], x["scale"], q_pe=x["q_pe"], k_pe=x["k_pe"])
+    O64c, lse64c = hp.oracle_forward_chunked(x, chunk=7, workers=3)
+    assert np.array_equal(O64, O64c) and np.array_equal(lse64, lse64c)
+    x["O"], x["lse"] = orc.emit_forward_outputs(O64, lse64)
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], x["scale"],
+                       q_pe=x["q_pe"], k_pe=x["k_pe"])
+    got = hp.oracle_backward_chunked(x, chunk=7, workers=3)
+    assert np.array_equal(got["dq"], ref["dq"]) and np.array_equal(got["dq_pe"], ref["dq_pe"])
+    for k in ("dkv", "dk_pe", "d_sink"):
+        np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-13, err_msg=k)
