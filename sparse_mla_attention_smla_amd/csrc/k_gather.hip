@@ -79,7 +79,10 @@ __global__ __launch_bounds__(kSegWaves * 64) void smla_k5_gather_segment(
     const int32_t* __restrict__ seg_row, int N, int64_t M, float* __restrict__ partial,
     uint16_t* __restrict__ dkv_single) {
     __shared__ float red[kSegWaves][kD];
-    const int s = blockIdx.x;
+    // segments from last to first: the pool rows (up to kGatherSeg contributors
+    // per segment, at the end of the row order) go out first and the short
+    // sliding-window segments fill the tail
+    const int s = gridDim.x - 1 - blockIdx.x;
     if (s >= seg_ptr[N]) return;  // grid is an upper bound on the segment count
     const int j = seg_row[s];
     const int beg = row_ptr[j] + (s - seg_ptr[j]) * kGatherSeg;  // plan checked the row's pointers

@@ -54,7 +54,10 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];  // two staging buffers
     __shared__ SlotList L;
 
-    const int t = blockIdx.x;
+    // tokens from last to first: the late tokens (the most valid slots) go out
+    // in the first rounds of workgroups, so the last round holds short ones,
+    // and the first tokens taken are the ones the dQ pass touched last
+    const int t = gridDim.x - 1 - blockIdx.x;
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, c16 = lane & 15, g = lane >> 4;

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(256) void smla_k5_gather_pe_segment(
     const int32_t* __restrict__ seg_row, int N, int64_t M, float* __restrict__ partial,
     uint16_t* __restrict__ dk_pe) {
     __shared__ float red[32][kDP + 4];
-    const int s = blockIdx.x;
+    const int s = gridDim.x - 1 - blockIdx.x;   // longest (pool-row) segments first, as the main gather
     if (s >= seg_ptr[N]) return;   // grid is an upper bound on the segment count
     const int j = seg_row[s];
     const int beg = row_ptr[j] + (s - seg_ptr[j]) * kGatherSeg;   // the plan checked the row's pointers
