@@ -46,7 +46,6 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     constexpr int R = 2 * H;
     constexpr int kYBytes = R * kYPitch;                 // one dsp block in LDS (padded rows)
     constexpr int kYChunks = R * kBK * 2 / 16;           // 16-B chunks of one dsp block
-    constexpr int kYPT = (kYChunks + kIThreads - 1) / kIThreads;
     static_assert(kYRing * kYBytes + 2 * kOBytes <= 2 * kStageBytes,
                   "Y ring and output buffers must fit in the staging area");
     constexpr int kPasses = (R + kStageRows - 1) / kStageRows;
@@ -117,17 +116,27 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 
     // ---- stream the Y tiles (one dsp block per compacted tile)
+    // Waves w and w+4 share a SIMD.  After each tile's barrier, waves 4-7 go
+    // straight to the next tile's MFMAs, while waves 0-3 first store the
+    // previous tile's output rows and bring the next dsp block into LDS, then
+    // run their MFMAs: each SIMD's MFMA pipe stays busy with one wave while the
+    // other does the tile's memory work (with every wave doing both, the pair
+    // did its memory work at the same time and left the pipe idle).
     const int ntk = (K + kBK - 1) / kBK;
     const uint16_t* ytok = dsp + (size_t)t * ntk * R * kBK;
+    constexpr int kSWaves = kIWaves / 2;                  // waves that stage and store
+    constexpr int kSThreads = kSWaves * 64;
+    constexpr int kYPS = (kYChunks + kSThreads - 1) / kSThreads;
+    const bool stager = w < kSWaves;
     // B operand: lane L of group g names Y row 32ks + 4g + L/4 (then +16),
     // columns 16sst + 4(L%4)
     const int yb = (4 * g + (c16 >> 2)) * kYPitch + (c16 & 3) * 8;
-    u32x4 pre[kYPT];
+    u32x4 pre[kYPS];
     auto load_tile = [&](int ct) {
         const uint16_t* src = ytok + (size_t)ct * R * kBK;
 #pragma unroll
-        for (int i = 0; i < kYPT; ++i) {
-            const int id = tid + kIThreads * i;
+        for (int i = 0; i < kYPS; ++i) {
+            const int id = tid + kSThreads * i;
             if (id < kYChunks) pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + id * 8));
         }
     };
@@ -135,8 +144,8 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // 16*(id/64) + id%16, positions 8g..8g+7 with g = (id/16)%4
     auto store_tile = [&](char* yb_lds) {
 #pragma unroll
-        for (int i = 0; i < kYPT; ++i) {
-            const int id = tid + kIThreads * i;
+        for (int i = 0; i < kYPS; ++i) {
+            const int id = tid + kSThreads * i;
             if (id < kYChunks)
                 *reinterpret_cast<u32x4*>(yb_lds + ((id >> 6) * 16 + (id & 15)) * kYPitch +
                                           ((id >> 4) & 3) * 16) = pre[i];
@@ -145,10 +154,23 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 
     // Output rows go out as buffer stores: the slot list decides the row, and a
     // lane whose position is past the last valid slot gets an offset past the
-    // token's range, which the hardware drops.  Every store is issued by every
-    // wave, so the compiler can count them when it waits for the Y prefetch.
+    // token's range, which the hardware drops.
     const __amdgpu_buffer_rsrc_t out_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         interm + (size_t)t * K * kD, (short)0, K * kD * 2, 0x00020000);
+    // whole 1 KiB rows of tile `it` leave with one non-temporal store each
+    // (staging wave w writes tile rows w, w+4, ...); row r is position r of the
+    // block, i.e. slot 4(r/8) + r%4 (+16 when r%8 >= 4) of the tile
+    auto store_rows = [&](int it, int n) {
+        const char* obuf = smem + kYRing * kYBytes + (it & 1) * kOBytes;
+#pragma unroll
+        for (int i = 0; i < kBK / kSWaves; ++i) {
+            const int r = w + kSWaves * i;
+            const int pos = it * kBK + ((r & 4) << 2) + ((r >> 3) << 2) + (r & 3);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(obuf + r * kOPitch + lane * 16);
+            const int voff = pos < n ? L.slot[pos] * (kD * 2) + lane * 16 : K * kD * 2;
+            __builtin_amdgcn_raw_buffer_store_b128(v, out_rsrc, voff, 0, kCacheNT);
+        }
+    };
     int ctg = 0;
     for (int k0 = 0; k0 < K; k0 += kChunk) {
         if (k0 > 0) {
@@ -158,19 +180,22 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         __syncthreads();
         const int n = L.n;
         const int ntile = (n + kBK - 1) / kBK;
-        if (ntile > 0) {
+        if (ntile > 0 && stager) {
             load_tile(ctg);
             store_tile(smem);
             if (ntile > 1) load_tile(ctg + 1);
         }
         __syncthreads();
         for (int it = 0; it < ntile; ++it) {
-            // tile it+1 (loaded during the previous iteration) goes to the ring slot
-            // that tile it-1 used; its loads are older than the previous
-            // iteration's stores, so waiting for them does not wait for those
-            if (it + 1 < ntile) {
-                store_tile(smem + ((it + 1) % kYRing) * kYBytes);
-                if (it + 2 < ntile) load_tile(ctg + it + 2);
+            if (stager) {
+                if (it > 0) store_rows(it - 1, n);
+                // tile it+1 (loaded during the previous iteration) goes to the ring
+                // slot that tile it-1 used; its loads are older than the row stores
+                // just issued, so waiting for them does not wait for those
+                if (it + 1 < ntile) {
+                    store_tile(smem + ((it + 1) % kYRing) * kYBytes);
+                    if (it + 2 < ntile) load_tile(ctg + it + 2);
+                }
             }
             const char* ybuf = smem + (it % kYRing) * kYBytes;
             char* obuf = smem + kYRing * kYBytes + (it & 1) * kOBytes;
@@ -199,18 +224,8 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                         u32x2{pack_bf16(cacc[dt][0], cacc[dt][1]), pack_bf16(cacc[dt][2], cacc[dt][3])};
             }
             __syncthreads();
-            // whole 1 KiB rows leave with one non-temporal store each (wave w
-            // writes tile rows w, w+8, w+16, w+24); row r is position r of the
-            // block, i.e. slot 4(r/8) + r%4 (+16 when r%8 >= 4) of the tile
-#pragma unroll
-            for (int i = 0; i < kBK / kIWaves; ++i) {
-                const int r = w + kIWaves * i;
-                const int pos = it * kBK + ((r & 4) << 2) + ((r >> 3) << 2) + (r & 3);
-                const u32x4 v = *reinterpret_cast<const u32x4*>(obuf + r * kOPitch + lane * 16);
-                const int voff = pos < n ? L.slot[pos] * (kD * 2) + lane * 16 : K * kD * 2;
-                __builtin_amdgcn_raw_buffer_store_b128(v, out_rsrc, voff, 0, kCacheNT);
-            }
         }
+        if (ntile > 0 && stager) store_rows(ntile - 1, n);
         ctg += ntile;
     }
 }
