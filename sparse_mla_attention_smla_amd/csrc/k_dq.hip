@@ -279,6 +279,7 @@ struct DqShared {
     int (*resc)[4];
     float (*alpha)[4][16];
     float (*oscale)[4][16];
+    char* pe_tiles;     // has_pe=True: ring slots of kPeTileBytes (positional key rows)
 };
 
 constexpr int kMinStream = 5;  // segments this long hand over to the next without a drain
@@ -320,18 +321,34 @@ __device__ __forceinline__ void settle_scalars(float a, float b) {
 // tile); the consumers accumulate O^T = kv^T . P^T and scale it by 1/sum in
 // their epilogue.  Then dO, delta and dsp are unused, lse is written (not
 // read), dq receives O, and the forward needs one segment per item (topk <= 512).
-template <bool PROD, bool FWD>
+//
+// PE adds the has_pe=True variant's positional part: the producers add
+// q_pe . k_pe^T to S^T (two more d-steps per 16-slot half, q_pe fragments in
+// registers), the consumers copy each tile's positional key rows into a second
+// ring and, in the backward, accumulate dq_pe^T = k_pe^T . (scale*dS)^T (16 of
+// its 64 columns each).  The ring is then 3 tiles deep instead of 4 so that
+// both rings fit in LDS: the stream only ever holds the consumers' tile, the
+// producers' tile and the one being copied.
+template <bool PROD, bool FWD, bool PE = false>
 __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                            const uint16_t* __restrict__ dO, const float* __restrict__ lse,
                                            const float* __restrict__ delta, const int32_t* __restrict__ idx,
                                            int T, int H, int N, int K, float scale, uint16_t* __restrict__ dq,
                                            uint16_t* __restrict__ dsp, const DqShared sh, int w, int lane,
                                            const float* __restrict__ sink = nullptr,
-                                           float* __restrict__ lse_out = nullptr) {
-    constexpr int R = kBK / 4;   // copies per consumer wave per tile
-    constexpr int kEpiStores = 32;  // global stores of one consumer epilogue (4 heads x 8 d-blocks)
+                                           float* __restrict__ lse_out = nullptr,
+                                           const uint16_t* __restrict__ q_pe = nullptr,
+                                           const uint16_t* __restrict__ k_pe = nullptr,
+                                           uint16_t* __restrict__ dq_pe = nullptr) {
+    constexpr int NB = PE ? 3 : kNBuf;           // ring depth
+    constexpr int kAhead = 2;                    // tiles copied ahead of the consumers
+    static_assert(NB > kAhead, "the ring holds the consumers', the producers' and the copied tile");
+    constexpr int R = kBK / 4 + (PE ? 1 : 0);    // copies per consumer wave per tile
+    // global stores of one consumer epilogue (4 heads x 8 d-blocks, + 4 of dq_pe)
+    constexpr int kEpiStores = 32 + (PE && !FWD ? 4 : 0);
     constexpr int kWarmTiles = 8;   // tiles over which the next item's q/dO are warmed (32 chunks)
     const int c16 = lane & 15, g = lane >> 4;
+    auto ring_slot = [](int pos) { return NB == 4 ? (pos & 3) : pos % NB; };
     const int nhg = H / 64;
     const ItemSeq seq(blockIdx.x, gridDim.x, T * nhg);
     const int spi = (K + kChunk - 1) / kChunk;   // segments per item
@@ -345,6 +362,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
 
     // ---------------------------------------------------------------- producer
     u32x4 qf[16], dof[16];
+    u32x4 qpf[2];                   // PE: q_pe B fragments (lane c16 + 16g: head c16, chunk g)
     float bias = 0.f, dl = 0.f;     // of the item being produced
     float nbias = 0.f, ndl = 0.f;   // of the next item, loaded with its q/dO
     // forward: bias/nbias hold the head's sink logit in log2 units (-inf: none);
@@ -371,6 +389,12 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         return ((size_t)t * H + hg * 64 + w * 16 + frag_load_lane_row(lane)) * kD +
                8 * frag_load_lane_chunk(lane);
     };
+    // PE: first element of this lane's q_pe fragment (loaded in MFMA order: 2 loads)
+    auto pe_src = [&](int item) {
+        int h; size_t lrow;
+        item_rows(item, h, lrow);
+        return lrow * kDP + 8 * g;
+    };
     auto load_item = [&](int item) {
         int h; size_t lrow;
         item_rows(item, h, lrow);
@@ -379,6 +403,11 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         for (int ds = 0; ds < 16; ++ds) {
             qf[ds] = *reinterpret_cast<const u32x4*>(q + src + 32 * ds);
             if constexpr (!FWD) dof[ds] = *reinterpret_cast<const u32x4*>(dO + src + 32 * ds);
+        }
+        if constexpr (PE) {
+            const size_t ps = pe_src(item);
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) qpf[s2] = *reinterpret_cast<const u32x4*>(q_pe + ps + 32 * s2);
         }
         if constexpr (FWD) {
             nbias = sink_of(h);
@@ -395,6 +424,10 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         frag_to_mfma_lanes(qf, lane);
         if constexpr (!FWD) frag_to_mfma_lanes(dof, lane);
         settle_scalars(nbias, ndl);
+        if constexpr (PE) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) asm volatile("" : : "v"(qpf[s2]));
+        }
     };
     // forward: lse of the item whose last tile was just produced (or that has no
     // valid slot), with the sink folded in; returns the output scale a/z of the head
@@ -430,8 +463,9 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     // S^T, dP^T of tile jt of the producer's segment (ring position pos) -> P,
     // scale*dS (stored) -> dS fragment into LDS.  With RELOAD, each d-chunk of
     // q/dO is replaced by the next item's right after its MFMAs.
-    auto produce = [&](int pos, int jt, auto reload, const uint16_t* nq, const uint16_t* nd) {
-        const char* buf = sh.tiles + (pos & (kNBuf - 1)) * kTileBytes;
+    auto produce = [&](int pos, int jt, auto reload, const uint16_t* nq, const uint16_t* nd,
+                       const uint16_t* nqp) {
+        const char* buf = sh.tiles + ring_slot(pos) * kTileBytes;
         const int rb = rows_base(c16, g);
         f32x4 sacc[2], pacc[2];
 #pragma unroll
@@ -464,6 +498,18 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             if constexpr (decltype(reload)::value) {
                 qf[ds] = *reinterpret_cast<const u32x4*>(nq + 32 * ds);
                 if constexpr (!FWD) dof[ds] = *reinterpret_cast<const u32x4*>(nd + 32 * ds);
+            }
+        }
+        if constexpr (PE) {
+            // positional part of S^T, then (reload) the next item's q_pe fragments
+            const char* pbuf = sh.pe_tiles + ring_slot(pos) * kPeTileBytes;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                for (int st = 0; st < 2; ++st) sacc[st] = mfma16(pe_rows_a(pbuf, c16, g, st, s2), qpf[s2], sacc[st]);
+            if constexpr (decltype(reload)::value) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) qpf[s2] = *reinterpret_cast<const u32x4*>(nqp + 32 * s2);
             }
         }
         if constexpr (FWD) {
@@ -539,18 +585,24 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     using Reload = std::integral_constant<bool, true>;
 
     // ---------------------------------------------------------------- consumer
-    const int dq4 = w - 4;  // d in [128 dq4, 128 dq4 + 128)
+    const int dq4 = w - 4;  // d in [128 dq4, 128 dq4 + 128) (dq_pe: [16 dq4, 16 dq4 + 16))
     const i32x4 rsrc = make_rsrc(kv, (uint32_t)N * (kD * 2));
-    f32x4 acc[8][4];
+    const i32x4 rsrc_pe = make_rsrc(k_pe, PE ? (uint32_t)N * kPeRow : 0u);
+    const uint32_t pe_ring = lds_addr(PE ? sh.pe_tiles : sh.tiles);
+    f32x4 acc[8][4], acc_pe[4];
     if constexpr (!PROD) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc[i][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc_pe[m] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     // consumer wave dq4 copies rows dq4, dq4 + 4, ... of tile ct of a slot list
+    // (PE: then positional copy dq4 of the four)
     auto issue = [&](const SlotList* L, int ct, int pos) {
-        issue_tile<4>(rsrc, L, ct, ring + (pos & (kNBuf - 1)) * kTileBytes, dq4, lane);
+        issue_tile<4>(rsrc, L, ct, ring + ring_slot(pos) * kTileBytes, dq4, lane);
+        if constexpr (PE) issue_pe_tile<4>(rsrc_pe, L, ct, pe_ring + ring_slot(pos) * kPeTileBytes, dq4, lane);
     };
     // Cache warming: during a segment's last tiles the consumers read the next
     // item's q and dO rows (64 KiB each, in 4 KiB chunks of 64 lines) into a
@@ -570,7 +622,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         u32x4 b[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) b[m] = sh.dsfrag[pos & 1][m][lane];
-        const char* buf = sh.tiles + (pos & (kNBuf - 1)) * kTileBytes;
+        const char* buf = sh.tiles + ring_slot(pos) * kTileBytes;
         // transposed kv reads two d-blocks ahead of their four MFMAs (pinned)
         u32x4 ca[8];
         ca[0] = tile_cols_a(buf, cb, 8 * dq4);
@@ -602,6 +654,11 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             if (dt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
+        if constexpr (PE && !FWD) {
+            const u32x4 pa = pe_cols_a(sh.pe_tiles + ring_slot(pos) * kPeTileBytes, pe_cols_base(c16, g), dq4);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) acc_pe[m] = mfma16(pa, b[m], acc_pe[m]);
+        }
     };
     // lane c16 + 16g holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16;
     // stored quad-contiguous (lane 4*c + g writes head 16m + c)
@@ -622,6 +679,14 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 *reinterpret_cast<u32x2*>(out + 16 * dt) =
                     to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane);
                 acc[dt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            if constexpr (PE && !FWD) {
+                // dq_pe^T rows 16dq4 + 4g .. +3 of head 16m + c16, stored quad-contiguous
+                uint16_t* op = dq_pe + ((size_t)t * H + h) * kDP + 16 * dq4 + 4 * (lane & 3);
+                const f32x4 v = acc_pe[m];
+                *reinterpret_cast<u32x2*>(op) =
+                    to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane);
+                acc_pe[m] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
     };
@@ -657,13 +722,13 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 enter_segment(s, first_of_item);
             } else {
 #pragma unroll
-                for (int p = 0; p < kNBuf - 2; ++p) issue(&Lb[s & 1], p, base + p);
+                for (int p = 0; p < kAhead; ++p) issue(&Lb[s & 1], p, base + p);
                 wait_vmcnt<R>();
                 since = 0;
             }
             __syncthreads();
             if constexpr (PROD) {
-                if (ntile > 0) produce(base, 0, NoReload{}, nullptr, nullptr);
+                if (ntile > 0) produce(base, 0, NoReload{}, nullptr, nullptr, nullptr);
             }
         }
         for (int j = 0; j < ntile; ++j) {
@@ -696,7 +761,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                         const int nitem = seg_item(s + 1);
                         item_rows(nitem, h, lrow);
                         const size_t src = frag_src(nitem);
-                        produce(pos + 1, j + 1, Reload{}, q + src, dO + src);
+                        produce(pos + 1, j + 1, Reload{}, q + src, dO + src, PE ? q_pe + pe_src(nitem) : nullptr);
                         if constexpr (FWD) {
                             nbias = sink_of(h);
                         } else {
@@ -705,17 +770,17 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                         }
                         finish_load();
                     } else {
-                        produce(pos + 1, j + 1, NoReload{}, nullptr, nullptr);
+                        produce(pos + 1, j + 1, NoReload{}, nullptr, nullptr, nullptr);
                     }
                 } else if (cont) {
                     if (!next_new_item) p_ctg += ntile;
                     enter_segment(s + 1, next_new_item);
-                    if (p_n > 0) produce(pos + 1, 0, NoReload{}, nullptr, nullptr);
+                    if (p_n > 0) produce(pos + 1, 0, NoReload{}, nullptr, nullptr, nullptr);
                 }
             } else {
-                const int ahead = j + kNBuf - 2;
-                if (ahead < ntile || !cont) issue(&Lb[s & 1], ahead, pos + kNBuf - 2);
-                else issue(&Lb[(s + 1) & 1], ahead - ntile, pos + kNBuf - 2);
+                const int ahead = j + kAhead;
+                if (ahead < ntile || !cont) issue(&Lb[s & 1], ahead, pos + kAhead);
+                else issue(&Lb[(s + 1) & 1], ahead - ntile, pos + kAhead);
                 {
                     const int first = ntile > kWarmTiles + 2 ? ntile - kWarmTiles - 2 : 0;
                     const bool warm = next_new_item && j >= first && j + 2 < ntile;
@@ -796,6 +861,55 @@ void smla_k7_fwd_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                                 lane, sink, lse);
 }
 
+// has_pe=True variants of the two persistent kernels: 3-deep kv ring plus the
+// positional ring (about 131 KiB of LDS).
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k2_dq_pc_pe(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                      const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                      const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
+                      int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp,
+                      const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe,
+                      uint16_t* __restrict__ dq_pe) {
+    __shared__ __attribute__((aligned(16))) char tiles[3 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char pe_tiles[3 * kPeTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    const DqShared sh{tiles, Lb, dsfrag, touch, nullptr, nullptr, nullptr, pe_tiles};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, false, true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane,
+                                      nullptr, nullptr, q_pe, k_pe, dq_pe);
+    else
+        dq_pc_role<false, false, true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane,
+                                       nullptr, nullptr, q_pe, k_pe, dq_pe);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k7_fwd_pc_pe(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                       const int32_t* __restrict__ idx, const float* __restrict__ sink, int T, int H,
+                       int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse,
+                       const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe) {
+    __shared__ __attribute__((aligned(16))) char tiles[3 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char pe_tiles[3 * kPeTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    __shared__ __attribute__((aligned(16))) int resc[2][4];
+    __shared__ float alpha[2][4][16];
+    __shared__ float oscale[2][4][16];
+    const DqShared sh{tiles, Lb, dsfrag, touch, resc, alpha, oscale, pe_tiles};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, true, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh, w,
+                                     lane, sink, lse, q_pe, k_pe, nullptr);
+    else
+        dq_pc_role<false, true, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh, w,
+                                      lane, sink, lse, q_pe, k_pe, nullptr);
+}
+
 hipError_t launch_fwd_pc(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
                          int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
                          hipStream_t s) {
@@ -840,12 +954,35 @@ hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, 
     return hipGetLastError();
 }
 
+hipError_t launch_fwd_pc_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                            const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
+                            uint16_t* o, float* lse, hipStream_t s) {
+    const int items = T * (H / 64);
+    int cus = 0;
+    const hipError_t e = compute_units(&cus);
+    if (e != hipSuccess) return e;
+    const unsigned blocks = (unsigned)(items < cus ? items : cus);
+    smla_k7_fwd_pc_pe<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe);
+    return hipGetLastError();
+}
+
 hipError_t launch_dq_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
                         const uint16_t* dO, const float* lse, const float* delta, const int32_t* idx, int T,
                         int H, int N, int K, float scale, uint16_t* dq, uint16_t* dq_pe, uint16_t* dsp,
                         hipStream_t s) {
     if (T == 0) return hipSuccess;
     const int nw = dq_waves(H);
+    if (nw == 4) {
+        // persistent, as for the plain op
+        const int items = T * (H / 64);
+        int cus = 0;
+        const hipError_t e = compute_units(&cus);
+        if (e != hipSuccess) return e;
+        const unsigned blocks = (unsigned)(items < cus ? items : cus);
+        smla_k2_dq_pc_pe<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, q_pe,
+                                                k_pe, dq_pe);
+        return hipGetLastError();
+    }
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
     switch (nw) {
         case 4:

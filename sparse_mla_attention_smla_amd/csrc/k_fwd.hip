@@ -180,10 +180,15 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
     return hipGetLastError();
 }
 
+hipError_t launch_fwd_pc_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                            const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
+                            uint16_t* o, float* lse, hipStream_t s);
+
 hipError_t launch_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
                          const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
                          uint16_t* o, float* lse, hipStream_t s) {
     if (T == 0) return hipSuccess;
+    if (H % 64 == 0 && K <= kChunk) return launch_fwd_pc_pe(q, q_pe, kv, k_pe, idx, sink, T, H, N, K, scale, o, lse, s);
     const int nw = dq_waves(H);
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
     switch (nw) {
