@@ -36,21 +36,38 @@ constexpr int kOPitch = 1040;                           // output row in LDS: 1 
 constexpr int kOBytes = kBK * kOPitch;                  // one tile of output rows
 }  // namespace
 
-// NKS = 2H / 32 reduction steps (H = 16 * NKS)
-template <int NKS>
+// NKS = 2H / 32 reduction steps (H = 16 * NKS).
+//
+// PE (the has_pe=True variant, H a multiple of 32) also forms the positional
+// intermediate interm_pe [T*topk, 64] = sum_h scale*dS . q_pe (bf16), from the
+// same dS fragments: q_pe_t is staged in LDS (rows 160 bytes apart) and each
+// MFMA-first wave 4 + e holds the transposed fragments of positional columns
+// 16e .. 16e+15 over the H dS rows (the first H/32 reduction steps), adds one
+// MFMA per such step, and stores its 16 columns of the tile's rows from a
+// small LDS tile at the next tile, whole 128-byte rows, one store per wave.
+template <int NKS, bool PE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kIThreads, kIThreads), amdgpu_waves_per_eu(2, 2)))
 void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dO,
                     const uint16_t* __restrict__ dsp, const int32_t* __restrict__ idx,
-                    int N, int K, uint16_t* __restrict__ interm) {
+                    int N, int K, uint16_t* __restrict__ interm,
+                    const uint16_t* __restrict__ q_pe, uint16_t* __restrict__ interm_pe) {
     constexpr int H = NKS * 16;
     constexpr int R = 2 * H;
     constexpr int kYBytes = R * kYPitch;                 // one dsp block in LDS (padded rows)
     constexpr int kYChunks = R * kBK * 2 / 16;           // 16-B chunks of one dsp block
-    static_assert(kYRing * kYBytes + 2 * kOBytes <= 2 * kStageBytes,
+    static_assert(!PE || NKS % 2 == 0, "the positional part needs H % 32 == 0");
+    constexpr int NKP = NKS / 2;                         // reduction steps over the dS rows
+    constexpr int kPeOPitch = kPeRow + 16;               // positional output row in LDS
+    constexpr int kPeOBytes = kBK * kPeOPitch;
+    static_assert(kYRing * kYBytes + 2 * kOBytes + (PE ? 2 * kPeOBytes : 0) <= 2 * kStageBytes,
                   "Y ring and output buffers must fit in the staging area");
     constexpr int kPasses = (R + kStageRows - 1) / kStageRows;
     constexpr int kRowsPerWave = kStageRows / kIWaves;   // row copies per wave per pass
+    constexpr int kXpPitch = kPeRow + 32;                // 160 B: odd multiple of 32
+    constexpr int kXpChunks = H * kDP * 2 / 16;          // 16-B chunks of q_pe_t
+    constexpr int kXpPerThread = (kXpChunks + kIThreads - 1) / kIThreads;
     __shared__ __attribute__((aligned(16))) char smem[2 * kStageBytes];  // two staging buffers
+    __shared__ __attribute__((aligned(16))) char xpe[PE ? H * kXpPitch : 16];
     __shared__ SlotList L;
 
     // tokens from last to first: the late tokens (the most valid slots) go out
@@ -81,6 +98,17 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             copy_row_to_lds_nt(is_q ? rq : rd, buf + r * kRowPitch, off);
         }
     };
+    // positional rows of the token, loaded first (older than every staging
+    // copy, so the waits below still count only copies) and written to LDS
+    // once the staging passes are through
+    u32x4 xpv[kXpPerThread];
+    if constexpr (PE) {
+#pragma unroll
+        for (int i = 0; i < kXpPerThread; ++i) {
+            const int id = tid + kIThreads * i;
+            if (id < kXpChunks) xpv[i] = *reinterpret_cast<const u32x4*>(q_pe + (size_t)t * H * kDP + id * 8);
+        }
+    }
     issue_pass(0);
     if (kPasses > 1) issue_pass(1);
     if (w == 0) compact_slots(idx_row, K, N, 0, &L, lane);
@@ -113,6 +141,26 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
         __syncthreads();
         if (p + 2 < kPasses) issue_pass(p + 2);
+    }
+    // xfp[ks] (waves 4-7, e = w - 4): positional column 16e + c16 of q_pe rows
+    // 32ks + 4g .. +3, then 32ks + 16 + 4g .. +3
+    u32x4 xfp[PE ? NKP : 1];
+    if constexpr (PE) {
+#pragma unroll
+        for (int i = 0; i < kXpPerThread; ++i) {
+            const int id = tid + kIThreads * i;
+            if (id < kXpChunks) *reinterpret_cast<u32x4*>(xpe + (id >> 3) * kXpPitch + (id & 7) * 16) = xpv[i];
+        }
+        __syncthreads();
+        if (w >= kIWaves / 2) {
+            const int xpb = (4 * g + (c16 >> 2)) * kXpPitch + (c16 & 3) * 8 + (w - kIWaves / 2) * 32;
+#pragma unroll
+            for (int ks = 0; ks < NKP; ++ks) {
+                const u32x2 lo = ds_read_tr16(xpe + xpb + 32 * ks * kXpPitch);
+                const u32x2 hi = ds_read_tr16(xpe + xpb + (32 * ks + 16) * kXpPitch);
+                xfp[ks] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+            }
+        }
     }
 
     // ---- stream the Y tiles (one dsp block per compacted tile)
@@ -160,6 +208,20 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     // whole 1 KiB rows of tile `it` leave with one non-temporal store each
     // (staging wave w writes tile rows w, w+4, ...); row r is position r of the
     // block, i.e. slot 4(r/8) + r%4 (+16 when r%8 >= 4) of the tile
+    // positional rows of tile `it`: wave 4 + e sends tile rows 8e .. 8e+7, 8
+    // lanes (16 bytes each) per 128-byte row
+    const __amdgpu_buffer_rsrc_t pe_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        PE ? interm_pe + (size_t)t * K * kDP : interm, (short)0, PE ? K * kPeRow : 0, 0x00020000);
+    auto store_pe_rows = [&](int it, int n) {
+        if constexpr (PE) {
+            const char* pbuf = smem + kYRing * kYBytes + 2 * kOBytes + (it & 1) * kPeOBytes;
+            const int r = 8 * (w - kIWaves / 2) + (lane >> 3);
+            const int pos = it * kBK + ((r & 4) << 2) + ((r >> 3) << 2) + (r & 3);
+            const u32x4 v = *reinterpret_cast<const u32x4*>(pbuf + r * kPeOPitch + (lane & 7) * 16);
+            const int voff = pos < n ? L.slot[pos] * kPeRow + (lane & 7) * 16 : K * kPeRow;
+            __builtin_amdgcn_raw_buffer_store_b128(v, pe_rsrc, voff, 0, kCacheNT);
+        }
+    };
     auto store_rows = [&](int it, int n) {
         const char* obuf = smem + kYRing * kYBytes + (it & 1) * kOBytes;
 #pragma unroll
@@ -187,6 +249,7 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         }
         __syncthreads();
         for (int it = 0; it < ntile; ++it) {
+            if (PE && !stager && it > 0) store_pe_rows(it - 1, n);
             if (stager) {
                 if (it > 0) store_rows(it - 1, n);
                 // tile it+1 (loaded during the previous iteration) goes to the ring
@@ -203,7 +266,7 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             for (int sst = 0; sst < 2; ++sst) {
                 // every B fragment (32 r x 16 slots) is read once and feeds the four
                 // d-blocks of this wave (four accumulation chains)
-                f32x4 cacc[4];
+                f32x4 cacc[4], cpe = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int dt = 0; dt < 4; ++dt) cacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -214,6 +277,18 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                     const u32x4 bfrag = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
                     for (int dt = 0; dt < 4; ++dt) cacc[dt] = mfma16(xf[dt][ks], bfrag, cacc[dt]);
+                    if constexpr (PE) {
+                        if (ks < NKP && !stager) cpe = mfma16(xfp[ks < NKP ? ks : 0], bfrag, cpe);
+                    }
+                }
+                if constexpr (PE) {
+                    // lane c16 + 16g: block position 16sst + c16, positional
+                    // columns 16e + 4g .. +3
+                    if (!stager) {
+                        char* prow = smem + kYRing * kYBytes + 2 * kOBytes + (it & 1) * kPeOBytes +
+                                     (16 * sst + c16) * kPeOPitch + ((w - kIWaves / 2) * 16 + 4 * g) * 2;
+                        *reinterpret_cast<u32x2*>(prow) = u32x2{pack_bf16(cpe[0], cpe[1]), pack_bf16(cpe[2], cpe[3])};
+                    }
                 }
                 // lane c16 + 16g holds slot it*32 + 16sst + c16, columns 64w + 16dt + 4g
                 // .. +3; the tile's output rows are assembled in LDS
@@ -226,6 +301,7 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             __syncthreads();
         }
         if (ntile > 0 && stager) store_rows(ntile - 1, n);
+        if (PE && ntile > 0 && !stager) store_pe_rows(ntile - 1, n);
         ctg += ntile;
     }
 }
@@ -235,7 +311,7 @@ hipError_t launch_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* 
                          hipStream_t s) {
     if (T == 0) return hipSuccess;
 #define SMLA_INTERM_CASE(nks) \
-    case nks: smla_k3_interm<nks><<<T, kIThreads, 0, s>>>(q, dO, dsp, idx, N, K, interm); break;
+    case nks: smla_k3_interm<nks, false><<<T, kIThreads, 0, s>>>(q, dO, dsp, idx, N, K, interm, nullptr, nullptr); break;
     switch (H / 16) {
         SMLA_INTERM_CASE(1)
         SMLA_INTERM_CASE(2)
@@ -248,6 +324,29 @@ hipError_t launch_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* 
         default: return hipErrorInvalidValue;
     }
 #undef SMLA_INTERM_CASE
+    return hipGetLastError();
+}
+
+}  // namespace smla
+
+namespace smla {
+
+hipError_t launch_interm_fused_pe(const uint16_t* q, const uint16_t* dO, const uint16_t* q_pe,
+                                  const uint16_t* dsp, const int32_t* idx, int T, int H, int N, int K,
+                                  uint16_t* interm, uint16_t* interm_pe, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+#define SMLA_INTERM_PE_CASE(nks)                                                                   \
+    case nks:                                                                                      \
+        smla_k3_interm<nks, true><<<T, kIThreads, 0, s>>>(q, dO, dsp, idx, N, K, interm, q_pe, interm_pe); \
+        break;
+    switch (H / 16) {
+        SMLA_INTERM_PE_CASE(2)
+        SMLA_INTERM_PE_CASE(4)
+        SMLA_INTERM_PE_CASE(6)
+        SMLA_INTERM_PE_CASE(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef SMLA_INTERM_PE_CASE
     return hipGetLastError();
 }
 

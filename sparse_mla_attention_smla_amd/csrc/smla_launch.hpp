@@ -82,6 +82,10 @@ hipError_t launch_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t
                          uint16_t* o, float* lse, hipStream_t s);
 hipError_t launch_interm_pe(const uint16_t* q_pe, const uint16_t* dsp, const int32_t* idx, int T, int H,
                             int N, int K, uint16_t* interm_pe, hipStream_t s);
+// both intermediates of the has_pe=True variant in one pass (H % 32 == 0)
+hipError_t launch_interm_fused_pe(const uint16_t* q, const uint16_t* dO, const uint16_t* q_pe,
+                                  const uint16_t* dsp, const int32_t* idx, int T, int H, int N, int K,
+                                  uint16_t* interm, uint16_t* interm_pe, hipStream_t s);
 size_t gather_pe_scratch_bytes(int64_t M, int N);
 // sums of the positional intermediate per kv row, over the segments of an
 // existing gather plan (launch_gather_plan on the same row_ptr)
