@@ -124,6 +124,7 @@ def _custom_pe(T, H, N, K, seed, sink=True, dup=False):
     (12, 64, 80, 600, True, True, False),    # topk beyond one index chunk
     (9, 128, 300, 96, True, False, True),    # most kv rows unused, dlse
     (17, 112, 30, 33, True, True, False),    # 7 head blocks of 16, 4 reduction steps with a half
+    (13, 96, 70, 100, False, True, True),    # 96 heads: fused intermediate with 3 positional steps
 ])
 def test_pe_ragged(T, H, N, K, sink, dup, with_dlse):
     _say(f"[pe ragged] T={T} H={H} N={N} K={K} sink={sink} dup={dup} dlse={with_dlse}")
@@ -161,3 +162,46 @@ def test_pe_zero_positional_parts_equal_the_plain_backward():
         _say(f"[pe zero] {name}: rel-L2 {rl:.1e} vs the plain backward, {100 * same:.2f}% bit-equal")
     assert_close("d_sink (q_pe = 0 vs plain)", got[4].cpu().numpy(), want[2].cpu().numpy(), tol=1e-6)
     assert torch.all(got[3].float() == 0)
+
+
+def test_pe_deterministic_and_graph_replays_match_eager():
+    """smla_bwd_pe twice gives the same bits; captured in a HIP graph (with its
+    helper-stream work folded onto the capturing stream), three replays with
+    eager work in between equal the eager call bit for bit."""
+    x = workload_pe("small", True)
+    d = _dev(x)
+    T, H, _ = x["q"].shape
+    N, K = x["kv"].shape[0], x["idx"].shape[1]
+    ws = torch.empty((B.bwd_pe_workspace_bytes(T, H, N, K),), dtype=torch.uint8, device="cuda")
+    first = _bwd(d, x, workspace=ws)
+    second = _bwd(d, x, workspace=ws)
+    for a, b, name in zip(first[:4], second[:4], ("dq", "dq_pe", "dkv", "dk_pe")):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{name} differs between runs"
+    assert torch.equal(first[4], second[4])
+    outs = (torch.empty_like(d["q"]), torch.empty_like(d["q_pe"]), torch.empty_like(d["kv"]),
+            torch.empty_like(d["k_pe"]), torch.empty_like(d["sink"]))
+
+    def call():
+        B.smla_bwd_pe(d["q"], d["q_pe"], d["kv"], d["k_pe"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"],
+                      x["scale"], workspace=ws, out=outs)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):       # warm-up call on the capture stream, outside capture
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in outs:
+            o.fill_(0)
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b, name in zip(outs[:4], first[:4], ("dq", "dq_pe", "dkv", "dk_pe")):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"replay {rep}: {name}"
+        assert torch.equal(outs[4], first[4]), f"replay {rep}: d_sink"
