@@ -259,7 +259,8 @@ struct ItemSeq {
 //     row copy, so each explicit vmcnt wait counts only that wave's own copies,
 //     warming copies and dq stores.
 // Producers run one tile ahead of consumers; one barrier per tile.  The tiles
-// of consecutive segments form one stream over the 4-deep ring: while segment
+// of consecutive segments form one stream over the ring (4 tiles deep; 3 in
+// the has_pe=True variant, whose positional ring takes the room): while segment
 // s ends, the first tiles of segment s+1 are already copied, its slot list
 // (double-buffered, built by producer 0 during segment s) is ready, its first tile
 // is produced, and for a new item the producers reload q and dO during their
@@ -268,7 +269,7 @@ struct ItemSeq {
 // Both roles run the same segment/tile control flow (same barrier sequence);
 // each role is its own instantiation so that only its state occupies registers.
 struct DqShared {
-    char* tiles;        // kNBuf ring slots of kTileBytes
+    char* tiles;        // ring slots of kTileBytes (kNBuf, or 3 with PE)
     SlotList* Lb;       // [2] slot lists, segment s uses Lb[s & 1]
     u32x4 (*dsfrag)[4][64];  // [2][4][64] dS (forward: P) fragments: [position parity][producer][lane]
     char* touch;             // 1 KiB landing area of the cache-warming copies (never read)

@@ -1,5 +1,7 @@
 // The has_pe=True variant's extra backward stages: the positional dKV
-// intermediate and its per-kv-row gather into dk_pe.
+// intermediate and its per-kv-row gather into dk_pe.  (For H a multiple of 32
+// the intermediate kernel of k_interm.hip forms the positional intermediate
+// itself; the kernel here serves the other head counts.)
 //
 // Page: aiter PR 4766 "Sparse MLA training backward", Contract section (the
 // op is the forward's has_pe=False path; has_pe=True is the forward's other
