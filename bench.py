@@ -9,7 +9,8 @@ O and lse are produced once by the library's own forward (smla_fwd).  The
 workspace and outputs are preallocated, so nothing is allocated while timing.
 
 Prints ONE JSON line: value = nominal TFLOPS (10*T*H*topk*512 flops per call,
-padded slots counted), ms_per_step, the roofline of the dominant kernel
+padded slots counted), ms_per_step, the skewed and long workloads timed the
+same way after it ("workloads"), the roofline of the dominant kernel
 (timed live inside the timed calls with HIP events that the library records on
 the calls' stream at its stage boundaries) and, on rank 0 at N=1, the fp64 CPU
 oracle timed on a bounded sample of the same workload.
@@ -38,8 +39,8 @@ D = 512
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--phased", choices=["on", "off"], default="off",
@@ -54,6 +55,10 @@ def parse():
     ap.add_argument("--stage-events", choices=["on", "off"], default="on",
                     help="time delta/dQ/intermediate/gather with events recorded inside the "
                          "timed calls (off: plain calls, stages timed through their entry points)")
+    ap.add_argument("--also", default="skewed,long",
+                    help="comma-separated workloads timed after the main one with plain smla_bwd "
+                         "calls (their own seeded inputs, O/lse from the library forward); '' for none")
+    ap.add_argument("--also-steps", type=int, default=20)
     ap.add_argument("--pe", choices=["on", "off"], default="on",
                     help="also time the has_pe=True variant (smla_fwd_pe, smla_bwd_pe) on the same "
                          "workload with seeded positional parts q_pe [T,H,64], k_pe [num_kv,64]")
@@ -228,6 +233,53 @@ def time_pe(B, w, q, kv, dO, idx, sink, reps):
             "fwd_ms": round(res["fwd"], 4), "fwd_tflops": round(fwd_flops / (res["fwd"] * 1e-3) / 1e12, 1),
             "note": "smla_bwd_pe / smla_fwd_pe with q_pe [T,H,64], k_pe [num_kv,64]; nominal flops "
                     "10*T*H*topk*512 + 6*T*H*topk*64 (backward), 4*T*H*topk*512 + 2*T*H*topk*64 (forward)"}
+
+
+def time_workload(B, name, steps, warmup):
+    """ms per plain smla_bwd call (median, p10, p90 of `steps` calls after `warmup`)
+    on another seeded workload, inputs resident, workspace and outputs preallocated."""
+    import numpy as np
+    import torch
+
+    from sparse_mla_attention_smla_amd import inputs
+    w = inputs.WORKLOADS[name]
+    T, H, N, K = w.T, w.H, w.num_kv, w.topk
+    print(f"[bench] generating {name}: T={T} H={H} num_kv={N} topk={K}", file=sys.stderr, flush=True)
+    x = inputs.make(name, sink=True)
+
+    def d16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    q, kv, dO = d16(x["q"]), d16(x["kv"]), d16(x["dO"])
+    idx = torch.from_numpy(x["idx"]).cuda()
+    sink = torch.from_numpy(x["sink"]).cuda()
+    nnz = int((x["idx"] >= 0).sum())
+    del x
+    scale = 1.0 / math.sqrt(D)
+    O, lse = B.smla_fwd(q, kv, idx, sink, scale)
+    outs = (torch.empty_like(q), torch.empty_like(kv), torch.empty(H, dtype=torch.float32, device="cuda"))
+    ws = torch.empty(B.bwd_workspace_bytes(T, H, N, K), dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        B.smla_bwd(q, kv, dO, O, lse, idx, sink, scale, workspace=ws, out=outs)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        B.smla_bwd(q, kv, dO, O, lse, idx, sink, scale, workspace=ws, out=outs)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    med = float(np.median(per))
+    print(f"[bench] {name}: {med:.3f} ms/call (median of {steps})", file=sys.stderr, flush=True)
+    row = {"ms_median": round(med, 4), "ms_p10": round(float(np.percentile(per, 10)), 4),
+           "ms_p90": round(float(np.percentile(per, 90)), 4),
+           "tflops": round(w.flops() / (med * 1e-3) / 1e12, 2),
+           "frac_of_bf16_peak": round(w.flops() / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+           "valid_slot_tflops": round(10.0 * nnz * H * D / (med * 1e-3) / 1e12, 2),
+           "steps": steps, "warmup": warmup,
+           "config": f"T={T} H={H} D={D} num_kv={N} topk={K}, {w.selection}, valid slots {nnz}"}
+    del q, kv, dO, idx, sink, O, lse, outs, ws
+    torch.cuda.empty_cache()
+    return row
 
 
 def cpu_baseline(w, n_tokens):
@@ -455,6 +507,12 @@ def main():
         print("[bench] has_pe variant", file=sys.stderr, flush=True)
         pe_row = time_pe(B, w, q, kv, dO, idx, sink, args.stage_steps)
 
+    # the other full-size workloads (parity-test configs) timed beside the main one
+    also_rows = {}
+    for name in [a.strip() for a in args.also.split(",") if a.strip()]:
+        if name != w.name:
+            also_rows[name] = time_workload(B, name, args.also_steps, 5)
+
     cpu = None
     if args.cpu_baseline == "on":
         print(f"[bench] cpu baseline: oracle on {args.cpu_sample_tokens} tokens", file=sys.stderr,
@@ -491,6 +549,7 @@ def main():
         "forward": forward,
         "phased": phased_row,
         "has_pe": pe_row,
+        "workloads": also_rows or None,
         "graph_replay": graph_row,
         "roofline": roofline,
         "cpu_baseline": cpu,
