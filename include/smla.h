@@ -26,18 +26,22 @@
  *    ranges must not overlap any other argument (else SMLA_ERR_INVALID_ARG).
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    work: they return without synchronising; results are ready when the
- *    stream reaches that point.  An eager smla_bwd / smla_bwd_phased call also
- *    uses one library-owned helper stream per device (default priority): it
- *    forks there with an event recorded on `stream` and joins back with an
- *    event that `stream` waits on, so all of its results are still ordered on
- *    `stream`.  When `stream` is being captured into a HIP graph, the call
- *    enqueues every stage on `stream` itself instead (same kernels, same
- *    results bit for bit), so the helper stream never joins a capture.  No
- *    hipMemset is enqueued (every output cell is written by a kernel).
- *    Calls from several host threads are safe, also while another thread
- *    captures: the library's enqueues are serialised by one mutex, and calls
- *    on different streams share only the helper stream (their work there runs
- *    in enqueue order; each call's buffers are its own).
+ *    stream reaches that point.  A smla_bwd / smla_bwd_phased / smla_bwd_pe
+ *    call also uses a library-owned helper stream (default priority): it forks
+ *    there with an event recorded on `stream` and joins back with an event
+ *    that `stream` waits on, so all of its results are still ordered on
+ *    `stream`.  Eager calls share one helper stream per device.  A call on a
+ *    stream that is being captured into a HIP graph uses a helper of that
+ *    capture's own (one of four per device, created by the first eager call):
+ *    the fork and join are captured with it, so eager calls of other threads
+ *    never enter the graph and two open captures never share a helper.  With
+ *    no such helper free, the captured call enqueues every stage on `stream`
+ *    itself (same kernels, same results bit for bit).  No hipMemset is
+ *    enqueued (every output cell is written by a kernel).  Calls from several
+ *    host threads are safe, also while other threads capture: the library's
+ *    enqueues are serialised by one mutex, and eager calls on different
+ *    streams share only the eager helper stream (their work there runs in
+ *    enqueue order; each call's buffers are its own).
  *  - Argument errors are reported synchronously before anything is enqueued.
  *    SMLA_ERR_ARCH is returned when the current device is not gfx950 (the
  *    page's wrapper likewise refuses other architectures).  A failed launch

@@ -75,11 +75,14 @@ struct SideStream {
     int state = 0;  // 0 not tried, 1 ready, 2 unavailable
 };
 SideStream g_side[kMaxDevices];
+// helper streams for calls under graph capture: each serves one open capture
+// at a time (it joins that capture through the fork event and leaves it when
+// the capture ends)
+constexpr int kCapSlots = 4;
+SideStream g_cap[kMaxDevices][kCapSlots];
 std::mutex g_side_mu;
 
-SideStream* side_stream(int dev) {
-    if (dev < 0 || dev >= kMaxDevices) return nullptr;
-    SideStream& d = g_side[dev];
+bool make_side(SideStream& d) {
     if (d.state == 0) {
         d.state = 2;
         if (hipStreamCreateWithFlags(&d.s, hipStreamNonBlocking) == hipSuccess &&
@@ -89,19 +92,44 @@ SideStream* side_stream(int dev) {
             hipEventCreateWithFlags(&d.gather_done, hipEventDisableTiming) == hipSuccess)
             d.state = 1;
     }
-    return d.state == 1 ? &d : nullptr;
+    return d.state == 1;
 }
 
-// The helper stream for a call on `s`, or nullptr when `s` is being captured
-// into a graph: then every stage is enqueued on `s` itself, so no
-// library-owned stream ever joins a capture (and eager calls from other
-// threads keep using the helper stream while the capture is open).  *err is
+// The eager helper stream of `dev`; its first use also creates the capture
+// helpers, so that no stream is ever created while a capture is open.
+SideStream* side_stream(int dev) {
+    if (dev < 0 || dev >= kMaxDevices) return nullptr;
+    for (int i = 0; i < kCapSlots; ++i) (void)make_side(g_cap[dev][i]);
+    return make_side(g_side[dev]) ? &g_side[dev] : nullptr;
+}
+
+// The helper stream for a call on `s`, or nullptr to enqueue every stage on
+// `s` itself.  Eager calls share the device's helper stream.  A call on a
+// stream being captured into a graph gets a capture helper of its own: the
+// one already joined to that capture (same capture id), else one that is in
+// no capture; so the eager helper never joins a capture, eager calls of other
+// threads never land in a graph, and two open captures never share a helper.
+// With no capture helper free (or none created yet: they are made by the first
+// eager call, never during a capture), the call runs in line on `s`.  *err is
 // set when the capture state cannot be read.
 SideStream* side_for(hipStream_t s, int dev, bool* err) {
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    *err = hipStreamIsCapturing(s, &cs) != hipSuccess;
-    if (*err || cs != hipStreamCaptureStatusNone) return nullptr;
-    return side_stream(dev);
+    unsigned long long id = 0;
+    *err = hipStreamGetCaptureInfo(s, &cs, &id) != hipSuccess;
+    if (*err) return nullptr;
+    if (cs == hipStreamCaptureStatusNone) return side_stream(dev);
+    if (cs != hipStreamCaptureStatusActive || dev < 0 || dev >= kMaxDevices) return nullptr;
+    SideStream* free_slot = nullptr;
+    for (int i = 0; i < kCapSlots; ++i) {
+        SideStream& c = g_cap[dev][i];
+        if (c.state != 1) continue;
+        hipStreamCaptureStatus cs2 = hipStreamCaptureStatusNone;
+        unsigned long long id2 = 0;
+        if (hipStreamGetCaptureInfo(c.s, &cs2, &id2) != hipSuccess) continue;
+        if (cs2 == hipStreamCaptureStatusActive && id2 == id) return &c;
+        if (cs2 == hipStreamCaptureStatusNone && free_slot == nullptr) free_slot = &c;
+    }
+    return free_slot;
 }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }

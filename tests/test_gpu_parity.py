@@ -361,6 +361,79 @@ def test_capture_on_one_thread_while_another_calls_eagerly(small_case):
             assert torch.equal(out_a[2], want[2]), rep
 
 
+def test_two_captures_open_at_once_and_two_calls_in_one_capture(small_case):
+    """Two threads each capture smla_bwd into their own graph while the other's
+    capture is open (each capture gets its own helper stream); thread A's graph
+    holds two calls (the second reuses the helper its capture already joined).
+    Every replay equals the eager results bit for bit."""
+    import threading
+    name, x, ref, d = small_case
+    T, H, _ = x["q"].shape
+    N, K = x["kv"].shape[0], x["idx"].shape[1]
+    d2 = dict(d)
+    d2["dO"] = (d["dO"].float() * 0.75).bfloat16()
+    want = (_run_bwd(d), _run_bwd(d2))
+    nbytes = B.bwd_workspace_bytes(T, H, N, K)
+    ws = [torch.empty((nbytes,), dtype=torch.uint8, device="cuda") for _ in range(3)]
+
+    def outs():
+        return (torch.empty_like(d["q"]), torch.empty_like(d["kv"]),
+                torch.empty_like(d["sink"]) if d["sink"] is not None else None)
+    out = [outs() for _ in range(3)]         # A: calls 0 (inputs d) and 1 (d2); B: call 2 (d2)
+    args = [d, d2, d2]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for i in range(3):                        # warm-up outside capture
+        with torch.cuda.stream(streams[0]):
+            a = args[i]
+            B.smla_bwd(a["q"], a["kv"], a["dO"], a["O"], a["lse"], a["idx"], a["sink"], SCALE,
+                       workspace=ws[i], out=out[i])
+    torch.cuda.synchronize()
+    graphs = [torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()]
+    barrier = threading.Barrier(2, timeout=120)
+    errors = []
+
+    def capture(k, calls):
+        # capture_begin/capture_end directly: the torch.cuda.graph context manager
+        # synchronises the device on entry, which another thread's open capture forbids
+        try:
+            with torch.cuda.stream(streams[k]):
+                graphs[k].capture_begin(capture_error_mode="thread_local")
+                try:
+                    barrier.wait()           # both captures are open from here
+                    for i in calls:
+                        a = args[i]
+                        B.smla_bwd(a["q"], a["kv"], a["dO"], a["O"], a["lse"], a["idx"], a["sink"], SCALE,
+                                   workspace=ws[i], out=out[i])
+                    barrier.wait()           # ... until both have enqueued their calls
+                finally:
+                    graphs[k].capture_end()
+        except BaseException as e:
+            errors.append(e)
+            barrier.abort()
+
+    ta = threading.Thread(target=capture, args=(0, (0, 1)))
+    tb = threading.Thread(target=capture, args=(1, (2,)))
+    ta.start(); tb.start()
+    ta.join(180); tb.join(180)
+    assert not ta.is_alive() and not tb.is_alive(), "capture threads did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for o in out:
+            o[0].fill_(0); o[1].fill_(0)
+        for w in ws:
+            w.fill_(0x3C)
+        torch.cuda.synchronize()
+        graphs[rep % 2].replay()
+        graphs[(rep + 1) % 2].replay()
+        torch.cuda.synchronize()
+        for i, wi in ((0, 0), (1, 1), (2, 1)):
+            for k in range(2):
+                assert torch.equal(host_bits_t(out[i][k]), host_bits_t(want[wi][k])), (rep, i, k)
+            if want[wi][2] is not None:
+                assert torch.equal(out[i][2], want[wi][2]), (rep, i)
+
+
 def test_binding_rejects_bad_outputs_and_workspaces():
     """Wrongly shaped, typed or placed outputs and workspaces raise before anything
     is enqueued; a workspace smaller than needed is reported by the library itself
