@@ -49,9 +49,8 @@ def parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=3072,
                     help="tokens of the oracle baseline sample (about 10 s of host work)")
     ap.add_argument("--stage-steps", type=int, default=10)
-    ap.add_argument("--graph", choices=["on", "off"], default="off",
-                    help="also time the call captured in a HIP graph and replayed (off by default "
-                         "so that the default run's kernel trace holds only the measured calls)")
+    ap.add_argument("--graph", choices=["on", "off"], default="on",
+                    help="also time the call captured in a HIP graph and replayed (graph_replay)")
     ap.add_argument("--stage-events", choices=["on", "off"], default="on",
                     help="time delta/dQ/intermediate/gather with events recorded inside the "
                          "timed calls (off: plain calls, stages timed through their entry points)")
@@ -158,8 +157,9 @@ def time_graph(w, step, reps):
         b.record(s)
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / reps
+    del g
     return {"ms": round(ms, 4), "tflops": round(w.flops() / (ms * 1e-3) / 1e12, 1),
-            "note": "the same call captured once in a HIP graph and replayed (launch gaps only differ)"}
+            "note": "the same call captured once in a HIP graph (with its own helper stream) and replayed; launch gaps only differ"}
 
 
 def time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq, dkv, ds, reps):
