@@ -145,6 +145,52 @@ def test_pe_ragged(T, H, N, K, sink, dup, with_dlse):
     assert np.max(np.abs(got_l[fin] - x["lse"][fin].astype(np.float64)), initial=0.0) < 1e-4
 
 
+def _fuzz_pe(seed):
+    """A random has_pe=True problem: any H the library takes, topk up to two index
+    chunks, slots drawn with replacement, -1 and out-of-range values anywhere;
+    the odd seeds have hundreds of tokens, so persistent workgroups take several
+    items and stream across them."""
+    rng = np.random.default_rng([91, seed])
+    T = int(rng.integers(300, 601)) if seed % 2 else int(rng.integers(1, 41))
+    H = int(rng.choice([16, 32, 48, 64, 80, 96, 112, 128]))
+    N = T + int(rng.integers(0, 160))
+    K = int(rng.choice([1, 16, 33, 64, 200, 512, 513, 600] if seed % 2 == 0 else [64, 200, 512]))
+    idx = rng.integers(0, N, size=(T, K)).astype(np.int32)
+    idx = np.where(rng.random((T, K)) < 0.25, -1, idx)
+    bad = rng.random((T, K)) < 0.02
+    idx = np.where(bad, np.where(rng.random((T, K)) < 0.5, -3, N + 9), idx).astype(np.int32)
+    s = 9000 + seed
+    x = {"q": inputs.normal_bf16((T, H, 512), s, 1), "kv": inputs.normal_bf16((N, 512), s, 2),
+         "dO": inputs.normal_bf16((T, H, 512), s, 3), "idx": idx,
+         "q_pe": inputs.normal_bf16((T, H, 64), s, 5), "k_pe": inputs.normal_bf16((N, 64), s, 6),
+         "sink": rng.standard_normal(H).astype(np.float32) if rng.integers(0, 2) else None,
+         "scale": SCALE_PE}
+    dlse = rng.standard_normal((T, H)).astype(np.float32) if rng.integers(0, 2) else None
+    return _with_forward(x), dlse
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_pe_random_problems(seed):
+    x, dlse = _fuzz_pe(seed)
+    T, H, _ = x["q"].shape
+    N, K = x["kv"].shape[0], x["idx"].shape[1]
+    _say(f"[pe fuzz {seed}] T={T} H={H} N={N} K={K} sink={x['sink'] is not None} dlse={dlse is not None}")
+    d = _dev(x)
+    o, lse = B.smla_fwd_pe(d["q"], d["q_pe"], d["kv"], d["k_pe"], d["idx"], d["sink"], x["scale"])
+    torch.cuda.synchronize()
+    assert_close("O (pe fuzz)", host_bf16(o), x["O64"])
+    got_l = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(x["lse"])
+    assert np.array_equal(np.isfinite(got_l), fin)
+    assert np.max(np.abs(got_l[fin] - x["lse"][fin].astype(np.float64)), initial=0.0) < 1e-4
+    got = _bwd(d, x, dlse=dlse, count_invalid=True)
+    assert int(got[5].item()) == orc.count_invalid(x["idx"], N)
+    ref = oracle_backward_chunked(x, dlse=dlse, chunk=16)
+    _check(f"pe fuzz {seed}", x, ref, got)
+    del d
+    torch.cuda.empty_cache()
+
+
 def test_pe_zero_positional_parts_equal_the_plain_backward():
     """q_pe = 0: every logit is the plain one, so smla_bwd_pe must give smla_bwd's
     dq, dkv and d_sink (the plain call may take another dQ kernel, so up to
