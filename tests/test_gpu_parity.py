@@ -612,6 +612,38 @@ def test_ragged_shapes(T, H, N, K, sink, with_dlse):
         assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
 
 
+def test_many_kv_rows_mostly_unused():
+    """num_kv in the hundreds of thousands with a few tokens: the CSR scans, the
+    gather plan and the row sums must cover every row (all but a few hundred of
+    them empty, so zero) and the used ones must match the oracle."""
+    T, H, N, K = 12, 16, 300_000, 32
+    rng = np.random.default_rng(4242)
+    idx = rng.integers(0, N, size=(T, K)).astype(np.int32)
+    idx = np.where(rng.random((T, K)) < 0.2, -1, idx).astype(np.int32)
+    x = {"q": inputs.normal_bf16((T, H, 512), 4242, 1), "kv": inputs.normal_bf16((N, 512), 4242, 2),
+         "dO": inputs.normal_bf16((T, H, 512), 4242, 3), "idx": idx,
+         "sink": rng.standard_normal(H).astype(np.float32)}
+    _say(f"[many kv] T={T} H={H} N={N} K={K}")
+    x = _oracle_inputs(x)
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE)
+    d = _to_dev(x)
+    dq, dkv, ds = _run_bwd(d)
+    assert_close("dq", host_bf16(dq), ref["dq"])
+    got = host_bf16(dkv)
+    used = np.unique(idx[idx >= 0])
+    assert_close("dkv (used rows)", got[used], ref["dkv"][used])
+    mask = np.ones(N, dtype=bool)
+    mask[used] = False
+    assert not np.any(got[mask]), "an unused kv row is not zero"
+    assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
+    row_ptr, slots = B.smla_build_csr(d["idx"], N)
+    rp, sl = orc.csr(idx, N)
+    assert np.array_equal(row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(slots.cpu().numpy()[: rp[-1]], sl)
+    del d, dq, dkv
+    torch.cuda.empty_cache()
+
+
 def _fuzz_case(seed):
     """A random small problem: any H the library takes, topk up to two index chunks,
     slots drawn with replacement (duplicate rows within a token), -1 padding and a
