@@ -101,11 +101,14 @@ def test_end_to_end_with_dlse(small_case):
 def test_stage_dq_and_dsp(small_case):
     name, x, ref, d = small_case
     delta = dev(ref["delta"].astype(np.float32))
-    dq, dsp = B.smla_dq(d["q"], d["kv"], d["dO"], d["lse"], delta, d["idx"], SCALE)
-    torch.cuda.synchronize()
-    assert_close(f"{name} dq stage", host_bf16(dq), ref["dq"])
     T, K = x["idx"].shape
     H = x["q"].shape[1]
+    # blocks past a token's last tile are never written: fill the buffer with 1.0
+    # first, so they hold finite values and an unwritten tail column would show
+    dsp_buf = torch.full((B.dsp_numel(T, H, K),), 1.0, dtype=torch.bfloat16, device="cuda")
+    dq, dsp = B.smla_dq(d["q"], d["kv"], d["dO"], d["lse"], delta, d["idx"], SCALE, dsp=dsp_buf)
+    torch.cuda.synchronize()
+    assert_close(f"{name} dq stage", host_bf16(dq), ref["dq"])
     ntk = (K + 31) // 32
     got = dsp_to_logical(host_bf16(dsp), H).reshape(T, ntk, 2 * H, 32)
     t, b, c, k = dsp_map(x["idx"], x["kv"].shape[0])
