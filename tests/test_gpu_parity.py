@@ -15,9 +15,9 @@ import pytest
 
 from oracle import smla_oracle as orc
 from sparse_mla_attention_smla_amd import inputs
-from tests._helpers import (SCALE, assert_close, dev, dev_bf16, dsp_from_logical, dsp_map,
-                            dsp_to_logical, full_reference, host_bf16, host_bits, rel_l2, workload,
-                            workload_nosink)
+from tests._helpers import (SCALE, _with_forward, assert_close, dev, dev_bf16, dsp_from_logical, dsp_map,
+                            dsp_to_logical, full_reference, host_bf16, host_bits, oracle_backward_chunked,
+                            rel_l2, workload, workload_nosink)
 
 pytestmark = pytest.mark.gpu
 
@@ -913,6 +913,39 @@ def _check_all_rows(name, x, ref, dq, dkv, ds):
     if x["sink"] is not None:
         r, c, worst = assert_close(f"{name} d_sink", ds.cpu().numpy(), ref["d_sink"])
         _say(f"[full] {name}: d_sink rel-L2 {r:.2e} worst head {worst:.2e}")
+
+
+# headline-like shapes that divide evenly nowhere: T = 3000 leaves the last round
+# of persistent dQ items ragged; 2500 tokens of 64 heads with topk 480 (15 tiles)
+_OTHER_SHAPES = {
+    "t3000": inputs.Workload("t3000", 20, T=3000, H=128, num_kv=3750, topk=512, selection="swa_pool",
+                             window=128, pool_stride=4, pool_picks=384),
+    "t2500_h64_k480": inputs.Workload("t2500_h64_k480", 21, T=2500, H=64, num_kv=3125, topk=480,
+                                      selection="swa_pool_zipf", window=128, pool_stride=4, pool_picks=352),
+}
+
+
+@pytest.mark.parametrize("name", sorted(_OTHER_SHAPES))
+def test_full_size_other_shapes_all_rows(name):
+    """Every dq row, dkv row and d_sink head against the oracle on seeded
+    headline-like workloads of other sizes; the CSR bit-exact."""
+    w = _OTHER_SHAPES[name]
+    _say(f"[full] {name}: T={w.T} H={w.H} num_kv={w.num_kv} topk={w.topk}")
+    x = _with_forward(inputs.make(w, sink=True))
+    d = _to_dev(x)
+    dq, dkv, ds = _run_bwd(d)
+    row_ptr, slots = B.smla_build_csr(d["idx"], w.num_kv)
+    rp, sl = orc.csr(x["idx"], w.num_kv)
+    assert np.array_equal(row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(slots.cpu().numpy()[: rp[-1]], sl)
+    _say(f"[full] {name}: oracle backward over all {w.T} tokens")
+    ref = oracle_backward_chunked(x)
+    _check_all_rows(name, x, ref, dq, dkv, ds)
+    o, lse = B.smla_fwd(d["q"], d["kv"], d["idx"], d["sink"], SCALE)
+    torch.cuda.synchronize()
+    assert_close(f"{name} O", host_bf16(o), x["O64"])
+    del d
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name,with_dlse", [("headline", False), ("skewed", False), ("long", False),
