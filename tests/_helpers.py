@@ -1,7 +1,8 @@
 """Shared test helpers: metrics, host<->device conversion, cached workloads.
 
 Inputs come from the seeded generator; O and lse from the oracle forward
-(rounded as the backward consumes them).  Nothing here computes attention.
+(rounded as the backward consumes them).  Nothing here computes attention; the
+rounding bounds below only sum magnitudes of products of the inputs.
 """
 from __future__ import annotations
 
@@ -74,6 +75,93 @@ def assert_close(name, got, want, tol=REL_L2, cos=COS, row_tol=ROW_REL):
                              f"errors {rows[bad].round(4).tolist()}; {int((rows > row_tol).sum())} rows "
                              f"over the bound of {rows.size})")
     return r, c, worst
+
+
+# fp32 unit roundoff for directed rounding: a bound that holds whichever rounding
+# the matrix cores' accumulation uses
+_U32 = 2.0 ** -23
+
+
+def cancellation_bounds(x, n=512):
+    """Per-element absolute bounds on dq (with the positional parts also dq_pe and
+    dk_pe) for a problem whose exact dS is zero on every valid slot: one unmasked
+    slot per token, no sink and no lse gradient give P = 1, so dS = P (dP - delta)
+    vanishes only because dP = <dO, kv_j> and delta = <dO, O> are equal (O is kv_j).
+    The library forms the two as fp32 sums of the same bf16 products in different
+    orders; each sum differs from its exact value by at most gamma_n = n u / (1 - n u)
+    times the sum of its products' magnitudes (recursive summation in any order),
+    so |dS| <= gamma_n (sum |dO kv_j| + sum |dO O|).  The outputs are scale times sums
+    of dS times |kv|, |k_pe| or |q_pe| (1% on top covers P's own rounding, the bf16
+    rounding of dS and of the output, and the fp32 sums over slots).  Masked slots
+    contribute nothing, so fully masked rows must come out exactly zero."""
+    kv, dO, O, idx = (np.asarray(x[k]) for k in ("kv", "dO", "O", "idx"))
+    kv64, dO64, O64 = (orc.bf16_to_f64(a) for a in (kv, dO, O))
+    T, H, _ = dO64.shape
+    N = kv64.shape[0]
+    scale = x.get("scale", SCALE)
+    g = n * _U32 / (1.0 - n * _U32)
+    valid = (idx >= 0) & (idx < N)
+    rows = np.where(valid, idx, 0)
+    sum_o = np.abs(dO64 * O64).sum(axis=2)                                   # [T, H]
+    out = {"dq": np.zeros((T, H, kv64.shape[1]))}
+    pe = "q_pe" in x
+    if pe:
+        kpe64, qpe64 = orc.bf16_to_f64(np.asarray(x["k_pe"])), orc.bf16_to_f64(np.asarray(x["q_pe"]))
+        out["dq_pe"] = np.zeros((T, H, kpe64.shape[1]))
+        out["dk_pe"] = np.zeros((N, kpe64.shape[1]))
+    for k in range(idx.shape[1]):
+        v = valid[:, k]
+        kvk = kv64[rows[:, k]]                                               # [T, 512]
+        b = g * (np.einsum("thd,td->th", np.abs(dO64), np.abs(kvk)) + sum_o) * v[:, None]
+        out["dq"] += b[:, :, None] * np.abs(kvk)[:, None, :]
+        if pe:
+            out["dq_pe"] += b[:, :, None] * np.abs(kpe64[rows[:, k]])[:, None, :]
+            np.add.at(out["dk_pe"], rows[v, k], np.einsum("th,thd->td", b[v], np.abs(qpe64[v])))
+    return {name: 1.01 * scale * a for name, a in out.items()}
+
+
+def assert_cancellation_zero(name, got, bound):
+    """A result whose exact value is zero through cancellation: every element
+    within its rounding bound (exactly zero where the bound is zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    over = np.abs(got) > bound
+    assert not over.any(), (f"{name}: {int(over.sum())} elements over the rounding bound, "
+                            f"worst |got| {np.abs(got).max():.3e}")
+    return float(np.abs(got).max(initial=0.0))
+
+
+# a whole reference tensor below this is no gradient of these inputs but a
+# cancellation: it is checked against the rounding bound instead of relatively
+_CANCEL_MAX = 1e-9
+
+
+def assert_close_or_cancelled(name, got, want, x, key):
+    """assert_close, unless the whole reference is zero through cancellation:
+    then the reference must itself sit at the fp64 level of the same bound
+    (2^-29 of the fp32 one), and the result within the fp32 bound of it."""
+    want = np.asarray(want, dtype=np.float64)
+    if np.abs(want).max(initial=0.0) > _CANCEL_MAX:
+        return assert_close(name, got, want)
+    b = cancellation_bounds(x)[key]
+    assert np.all(np.abs(want) <= b * 2.0 ** -29), f"{name}: tiny reference is no cancellation"
+    assert_cancellation_zero(name, got, b + np.abs(want))
+    return None
+
+
+def single_slot_problem(T, H, N, pe, seed):
+    """One valid slot per token (token 3 fully masked, token T//2 out of range,
+    rows drawn with replacement), no sink: P = 1 on every valid slot, so dq (and
+    dq_pe, dk_pe) are zero through cancellation.  With the oracle forward's O, lse."""
+    rng = np.random.default_rng([seed, T, H, N])
+    idx = rng.integers(0, N, size=(T, 1)).astype(np.int32)
+    idx[min(3, T - 1)] = -1
+    idx[T // 2] = N + 4
+    x = {"q": inputs.normal_bf16((T, H, 512), seed, 1), "kv": inputs.normal_bf16((N, 512), seed, 2),
+         "dO": inputs.normal_bf16((T, H, 512), seed, 3), "idx": idx, "sink": None, "scale": SCALE}
+    if pe:
+        x["q_pe"], x["k_pe"] = inputs.normal_bf16((T, H, 64), seed, 5), inputs.normal_bf16((N, 64), seed, 6)
+        x["scale"] = SCALE_PE
+    return _with_forward(x)
 
 
 def oracle_backward_chunked(x, dlse=None, chunk=32, workers=None):

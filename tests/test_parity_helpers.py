@@ -89,3 +89,42 @@ def test_chunked_oracle_with_positional_parts():
     assert np.array_equal(got["dq"], ref["dq"]) and np.array_equal(got["dq_pe"], ref["dq_pe"])
     for k in ("dkv", "dk_pe", "d_sink"):
         np.testing.assert_allclose(got[k], ref[k], rtol=1e-12, atol=1e-13, err_msg=k)
+
+
+@pytest.mark.parametrize("pe", [False, True])
+def test_cancellation_bound_admits_fp32_reorderings_and_catches_a_dropped_delta(pe):
+    """The bound for results that are zero only through cancellation: dq from an
+    fp32 emulation in which dP and delta are summed in two different orders
+    stays within it (exactly zero on masked tokens), the oracle's own result sits
+    at its fp64 level, and a dS that drops delta, or takes it from a wrong row,
+    lands far outside."""
+    x = hp.single_slot_problem(24, 16, 40, pe, seed=71)
+    ref = hp.oracle_backward_chunked(x, chunk=8, workers=2)
+    b = hp.cancellation_bounds(x)
+    keys = ("dq", "dq_pe", "dk_pe") if pe else ("dq",)
+    for k in keys:
+        assert np.all(np.abs(ref[k]) <= b[k] * 2.0 ** -29), k
+    assert np.all(b["dq"][[3, 12]] == 0.0)
+    kv = orc.bf16_to_f64(x["kv"]).astype(np.float32)
+    dO = orc.bf16_to_f64(x["dO"]).astype(np.float32)
+    O = orc.bf16_to_f64(x["O"]).astype(np.float32)
+    j = np.clip(x["idx"][:, 0], 0, kv.shape[0] - 1)
+    valid = (x["idx"][:, 0] >= 0) & (x["idx"][:, 0] < kv.shape[0])
+    dP = np.einsum("thd,td->th", dO, kv[j]).astype(np.float32)              # one summation order
+    delta = np.zeros(dO.shape[:2], dtype=np.float32)
+    for d in range(511, -1, -1):                                             # another: sequential, reversed
+        delta = (delta + dO[:, :, d] * O[:, :, d]).astype(np.float32)
+    scale = np.float32(x["scale"])
+
+    def dq_of(ds):
+        ds = np.where(valid[:, None], ds, 0.0).astype(np.float32)
+        return (scale * ds[:, :, None] * kv[j][:, None, :]).astype(np.float64)
+
+    emul = dq_of(dP - delta)
+    assert np.abs(emul).max() > 0.0                                          # the orders do differ
+    hp.assert_cancellation_zero("fp32 emulation", emul, b["dq"])
+    hp.assert_close_or_cancelled("fp32 emulation", emul, ref["dq"], x, "dq")
+    assert b["dq"].max() < 1e-2
+    for wrong in (dP, dP - np.roll(delta, 1, axis=0)):
+        with pytest.raises(AssertionError, match="over the rounding bound"):
+            hp.assert_cancellation_zero("planted", dq_of(wrong), b["dq"])
