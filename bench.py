@@ -187,9 +187,9 @@ def time_phased(B, w, q, kv, dO, O, lse, idx, sink, scale, ph_tokens, ws, dq, dk
             "full_workspace_gib": round(ws.numel() / 2 ** 30, 3)}
 
 
-def time_pe(B, w, q, kv, dO, idx, sink, reps):
+def time_pe(B, w, q, kv, dO, idx, sink, reps, warmup):
     """The has_pe=True variant on the same workload: ms per smla_bwd_pe call and per
-    smla_fwd_pe call, with seeded positional parts (scale 1/sqrt(512 + 64))."""
+    smla_fwd_pe call (medians), with seeded positional parts (scale 1/sqrt(512 + 64))."""
     import numpy as np
     import torch
 
@@ -214,25 +214,32 @@ def time_pe(B, w, q, kv, dO, idx, sink, reps):
 
     res = {}
     for name, fn in (("bwd", bwd), ("fwd", fwd)):
-        fn()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
+        # as for the other workloads: warm-up calls (the clock settles over the
+        # first few tens of calls after an idle spell), then each call timed alone
+        for _ in range(warmup):
             fn()
-        b.record()
         torch.cuda.synchronize()
-        res[name] = a.elapsed_time(b) / reps
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        res[name] = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)])
     # nominal flops: the plain op's plus the positional products (S, dq_pe and the
     # positional intermediate in the backward; S in the forward), 64 wide
     bwd_flops = w.flops() + 6.0 * T * H * K * 64
     fwd_flops = 4.0 * T * H * K * D + 2.0 * T * H * K * 64
     del ws
-    return {"bwd_ms": round(res["bwd"], 4), "bwd_tflops": round(bwd_flops / (res["bwd"] * 1e-3) / 1e12, 1),
-            "bwd_frac_of_bf16_peak": round(bwd_flops / (res["bwd"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "fwd_ms": round(res["fwd"], 4), "fwd_tflops": round(fwd_flops / (res["fwd"] * 1e-3) / 1e12, 1),
-            "note": "smla_bwd_pe / smla_fwd_pe with q_pe [T,H,64], k_pe [num_kv,64]; nominal flops "
-                    "10*T*H*topk*512 + 6*T*H*topk*64 (backward), 4*T*H*topk*512 + 2*T*H*topk*64 (forward)"}
+    bms, fms = float(np.median(res["bwd"])), float(np.median(res["fwd"]))
+    return {"bwd_ms": round(bms, 4), "bwd_ms_p10": round(float(np.percentile(res["bwd"], 10)), 4),
+            "bwd_ms_p90": round(float(np.percentile(res["bwd"], 90)), 4),
+            "bwd_tflops": round(bwd_flops / (bms * 1e-3) / 1e12, 1),
+            "bwd_frac_of_bf16_peak": round(bwd_flops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "fwd_ms": round(fms, 4), "fwd_tflops": round(fwd_flops / (fms * 1e-3) / 1e12, 1),
+            "note": f"smla_bwd_pe / smla_fwd_pe with q_pe [T,H,64], k_pe [num_kv,64]; median of {reps} calls "
+                    f"after {warmup} warm-up calls; nominal flops 10*T*H*topk*512 + 6*T*H*topk*64 (backward), "
+                    "4*T*H*topk*512 + 2*T*H*topk*64 (forward)"}
 
 
 def time_workload(B, name, steps, warmup):
@@ -505,7 +512,7 @@ def main():
     pe_row = None
     if args.pe == "on":
         print("[bench] has_pe variant", file=sys.stderr, flush=True)
-        pe_row = time_pe(B, w, q, kv, dO, idx, sink, args.stage_steps)
+        pe_row = time_pe(B, w, q, kv, dO, idx, sink, args.also_steps, 10)
 
     # the other full-size workloads (parity-test configs) timed beside the main one
     also_rows = {}

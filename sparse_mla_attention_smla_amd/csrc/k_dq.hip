@@ -80,7 +80,7 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
     const i32x4 rsrc_pe = make_rsrc(k_pe, PE ? (uint32_t)N * kPeRow : 0u);
     const uint32_t ring = lds_addr(tiles);
     const uint32_t pe_ring = lds_addr(pe_tiles);
-    const int rb = rows_base(c16, g), cb = cols_base(c16, g), pcb = pe_cols_base(c16, g);
+    const int rb = rows_base(c16, g), cb = cols_base(c16, g);
     const int ntk = (K + kBK - 1) / kBK;
     uint16_t* dsp_tok = dsp + (size_t)t * ntk * (2 * H) * kBK;
 
@@ -108,7 +108,7 @@ void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
         if constexpr (PE) {
             const char* pbuf = pe_tiles + slot * kPeTileBytes;
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc_pe[dt] = mfma16(pe_cols_a(pbuf, pcb, dt), bf, acc_pe[dt]);
+            for (int dt = 0; dt < 4; ++dt) acc_pe[dt] = mfma16(pe_cols_a(pbuf, c16, g, dt), bf, acc_pe[dt]);
         }
     };
 
@@ -656,7 +656,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         if constexpr (PE && !FWD) {
-            const u32x4 pa = pe_cols_a(sh.pe_tiles + ring_slot(pos) * kPeTileBytes, pe_cols_base(c16, g), dq4);
+            const u32x4 pa = pe_cols_a(sh.pe_tiles + ring_slot(pos) * kPeTileBytes, c16, g, dq4);
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc_pe[m] = mfma16(pa, b[m], acc_pe[m]);
         }

@@ -190,13 +190,22 @@ __device__ __forceinline__ u32x4 tile_cols_a(const char* buf, int base, int dt) 
 
 // ---- positional key rows (the has_pe=True variant) ------------------------
 // A head-shared positional key part of kDP = 64 bf16 (128 bytes) per kv row.
-// A tile's 32 rows sit contiguously in LDS ([32][64], 4 KiB), written by four
-// 1 KiB buffer->LDS copies: copy c covers tile rows 8c..8c+7, lane l fetching
-// 16-byte chunk l%8 of row 8c + l/8 (so the LDS image is the rows back to
-// back).  Tail positions fetch from past the buffer's range and land as zeros.
+// A tile's 32 rows take 4 KiB of LDS in four 1 KiB blocks, block c holding
+// tile rows 8c..8c+7 and written by one buffer->LDS copy (lane l lands at byte
+// 16 l of the block).  Inside a block, 16-byte chunk k (0..7) of row r (0..7)
+// sits at chunk slot pe_slot(r, k) = 16 (r % 4) + (2 r + k) % 16.  That is a
+// bijection on the block's 64 slots (for each value of (2 r + k) % 16 exactly
+// one of r, r + 4 has k <= 7), and it puts every byte at the same address
+// modulo 256 as rows 32 bytes (mod 256) apart would, the kv tiles' pitch
+// above: both operand reads below then meet the banks as the kv reads do,
+// where plain back-to-back 128-byte rows are several-way conflicted.  Lane l
+// of a copy fetches the chunk its slot holds; tail positions fetch from past
+// the buffer's range and land as zeros.
 constexpr int kDP = 64;
 constexpr int kPeRow = kDP * 2;              // 128 bytes
 constexpr int kPeTileBytes = kBK * kPeRow;   // 4,096 bytes
+
+__device__ __forceinline__ int pe_slot(int r, int k) { return 16 * (r & 3) + ((2 * r + k) & 15); }
 
 // Copies of positional tile `ct` issued by wave w of NW (NW in {1, 2, 4}):
 // copies w, w + NW, ... of the four, i.e. exactly 4/NW per wave.
@@ -206,29 +215,34 @@ __device__ __forceinline__ void issue_pe_tile(i32x4 rsrc, const SlotList* L, int
     static_assert(NW == 1 || NW == 2 || NW == 4, "four copies split evenly over the waves");
     constexpr int kP = 4 / NW;
     const int n = L->n;
+    // the (row, chunk) of the block that slot `lane` holds (inverse of pe_slot)
+    const int k0 = ((lane & 15) - 2 * (lane >> 4)) & 15;
+    const int r = (lane >> 4) + ((k0 >> 3) << 2), k = k0 & 7;
 #pragma unroll
     for (int i = 0; i < kP; ++i) {
         const int c = w + NW * i;
-        const int pos = ct * kBK + 8 * c + (lane >> 3);
+        const int pos = ct * kBK + 8 * c + r;
         const int rowv = L->row[pos < kChunk ? pos : kChunk - 1];
         const int row = pos < n ? rowv : kOobRow;
-        copy_row_to_lds(rsrc, buf + c * 1024, row * kPeRow + (lane & 7) * 16);
+        copy_row_to_lds(rsrc, buf + c * 1024, row * kPeRow + k * 16);
     }
 }
 
 // S^T A operand of the positional part: lane (c16, g) reads tile row
-// 16*st + c16, positional elements 32*s + 8g .. +7 (s = 0, 1).
+// 16*st + c16, positional elements 32*s + 8g .. +7 (chunk 4s + g; s = 0, 1).
 __device__ __forceinline__ u32x4 pe_rows_a(const char* buf, int c16, int g, int st, int s) {
-    return *reinterpret_cast<const u32x4*>(buf + (16 * st + c16) * kPeRow + s * 64 + g * 16);
+    return *reinterpret_cast<const u32x4*>(buf + (2 * st + (c16 >> 3)) * 1024 + 16 * pe_slot(c16 & 7, 4 * s + g));
 }
 
 // Transposed A operand of dq_pe^T = kpe_tile^T . dS^T for positional d-tile dt
-// (dt = 0..3): the same lane pattern as tile_cols_a with the 128-byte pitch.
-__device__ __forceinline__ int pe_cols_base(int c16, int g) { return (4 * g + (c16 >> 2)) * kPeRow + (c16 & 3) * 8; }
-
-__device__ __forceinline__ u32x4 pe_cols_a(const char* buf, int base, int dt) {
-    const u32x2 lo = ds_read_tr16(buf + base + dt * 32);
-    const u32x2 hi = ds_read_tr16(buf + base + 16 * kPeRow + dt * 32);
+// (dt = 0..3): the lane pattern of tile_cols_a, lane (c16, g) naming row
+// 4g + c16/4 (then 16 more) and elements 16dt + 4(c16%4) .. +3, i.e. half
+// c16 % 2 of chunk 2dt + (c16 % 4)/2.
+__device__ __forceinline__ u32x4 pe_cols_a(const char* buf, int c16, int g, int dt) {
+    const int r = 4 * g + (c16 >> 2);
+    const char* p = buf + (r >> 3) * 1024 + 16 * pe_slot(r & 7, 2 * dt + ((c16 & 3) >> 1)) + 8 * (c16 & 1);
+    const u32x2 lo = ds_read_tr16(p);
+    const u32x2 hi = ds_read_tr16(p + 2048);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
