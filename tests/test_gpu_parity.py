@@ -668,7 +668,7 @@ def _fuzz_case(seed):
     return x, dlse
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_random_problems(seed):
     x, dlse = _fuzz_case(seed)
     T, H, _ = x["q"].shape
