@@ -936,8 +936,12 @@ def _check_all_rows(name, x, ref, dq, dkv, ds):
 
 
 # headline-like shapes that divide evenly nowhere: T = 3000 leaves the last round
-# of persistent dQ items ragged; 2500 tokens of 64 heads with topk 480 (15 tiles)
+# of persistent dQ items ragged; 2500 tokens of 64 heads with topk 480 (15 tiles);
+# 16384 tokens of 16 heads put 8 GiB in the intermediate, so its rows, the dS/P
+# blocks and the CSR slot ids of the later tokens sit past 2^32 bytes
 _OTHER_SHAPES = {
+    "t16384_h16": inputs.Workload("t16384_h16", 22, T=16384, H=16, num_kv=20480, topk=512, selection="swa_pool",
+                                  window=128, pool_stride=4, pool_picks=384),
     "t3000": inputs.Workload("t3000", 20, T=3000, H=128, num_kv=3750, topk=512, selection="swa_pool",
                              window=128, pool_stride=4, pool_picks=384),
     "t2500_h64_k480": inputs.Workload("t2500_h64_k480", 21, T=2500, H=64, num_kv=3125, topk=480,
