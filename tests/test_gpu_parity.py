@@ -615,14 +615,17 @@ def test_ragged_shapes(T, H, N, K, sink, with_dlse):
         assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
 
 
-def test_many_kv_rows_mostly_unused():
-    """num_kv in the hundreds of thousands with a few tokens: the CSR scans, the
-    gather plan and the row sums must cover every row (all but a few hundred of
-    them empty, so zero) and the used ones must match the oracle."""
-    T, H, N, K = 12, 16, 300_000, 32
+@pytest.mark.parametrize("N", [300_000, (1 << 20) - 1])
+def test_many_kv_rows_mostly_unused(N):
+    """num_kv in the hundreds of thousands, up to the largest the library takes,
+    with a few tokens: the CSR scans, the gather plan and the row sums must cover
+    every row (all but a few hundred of them empty, so zero) and the used ones,
+    the first and the last row among them, must match the oracle."""
+    T, H, K = 12, 16, 32
     rng = np.random.default_rng(4242)
     idx = rng.integers(0, N, size=(T, K)).astype(np.int32)
     idx = np.where(rng.random((T, K)) < 0.2, -1, idx).astype(np.int32)
+    idx[0, 0], idx[1, 0], idx[2, 5] = N - 1, 0, N - 1
     x = {"q": inputs.normal_bf16((T, H, 512), 4242, 1), "kv": inputs.normal_bf16((N, 512), 4242, 2),
          "dO": inputs.normal_bf16((T, H, 512), 4242, 3), "idx": idx,
          "sink": rng.standard_normal(H).astype(np.float32)}
