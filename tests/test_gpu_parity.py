@@ -650,6 +650,48 @@ def test_many_kv_rows_mostly_unused(N):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("H", [64, 16])
+def test_very_large_topk(H):
+    """topk = 65536: 128 index chunks per token, so a dQ item streams through 128
+    segments and the forward through as many chunks; slots drawn with
+    replacement from 70,000 rows, a quarter masked, one token with only three
+    valid slots.  Backward against the oracle (dkv on the used rows, the rest
+    exactly zero), the CSR bit-exact, the forward's O and lse."""
+    T, N, K = 3, 70_000, 1 << 16
+    rng = np.random.default_rng(6500 + H)
+    idx = rng.integers(0, N, size=(T, K)).astype(np.int32)
+    idx = np.where(rng.random((T, K)) < 0.25, -1, idx).astype(np.int32)
+    idx[1] = -1
+    idx[1, [7, 40000, K - 1]] = [5, N - 1, 5]
+    x = {"q": inputs.normal_bf16((T, H, 512), 6500 + H, 1), "kv": inputs.normal_bf16((N, 512), 6500 + H, 2),
+         "dO": inputs.normal_bf16((T, H, 512), 6500 + H, 3), "idx": idx,
+         "sink": rng.standard_normal(H).astype(np.float32)}
+    _say(f"[large topk] T={T} H={H} N={N} K={K}")
+    x = _oracle_inputs(x)
+    d = _to_dev(x)
+    dq, dkv, ds = _run_bwd(d)
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE)
+    assert_close("dq", host_bf16(dq), ref["dq"])
+    got = host_bf16(dkv)
+    used = np.unique(idx[idx >= 0])
+    assert_close("dkv (used rows)", got[used], ref["dkv"][used])
+    mask = np.ones(N, dtype=bool)
+    mask[used] = False
+    assert not np.any(got[mask]), "an unused kv row is not zero"
+    assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
+    row_ptr, slots = B.smla_build_csr(d["idx"], N)
+    rp, sl = orc.csr(idx, N)
+    assert np.array_equal(row_ptr.cpu().numpy(), rp)
+    assert np.array_equal(slots.cpu().numpy()[: rp[-1]], sl)
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    o, lse = B.smla_fwd(d["q"], d["kv"], d["idx"], d["sink"], SCALE)
+    torch.cuda.synchronize()
+    assert_close("O", host_bf16(o), O64)
+    assert np.max(np.abs(lse.cpu().numpy().astype(np.float64) - lse64)) < 1e-4
+    del d, dq, dkv
+    torch.cuda.empty_cache()
+
+
 def _fuzz_case(seed):
     """A random small problem: any H the library takes, topk up to two index chunks,
     slots drawn with replacement (duplicate rows within a token), -1 padding and a
