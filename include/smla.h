@@ -24,6 +24,12 @@
  *  - 16-byte alignment is required for bf16 tensors and the workspace, 4-byte
  *    for float/int32 tensors (else SMLA_ERR_ALIGN).  Output and workspace
  *    ranges must not overlap any other argument (else SMLA_ERR_INVALID_ARG).
+ *  - Every pointer must be device (or managed) memory of the current device;
+ *    host memory, pinned or not, and other devices' memory are refused with
+ *    SMLA_ERR_INVALID_ARG before anything is enqueued.  The first and last
+ *    byte of each argument's range are checked, so a buffer shorter than its
+ *    range is also refused when the bytes past its end are not this device's
+ *    memory.
  *  - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue
  *    work: they return without synchronising; results are ready when the
  *    stream reaches that point.  A smla_bwd / smla_bwd_phased / smla_bwd_pe
@@ -61,7 +67,8 @@ extern "C" {
 
 typedef enum {
     SMLA_OK = 0,
-    SMLA_ERR_INVALID_ARG = 1, /* null pointer, overlap, non-finite scale, sink/d_sink mismatch */
+    SMLA_ERR_INVALID_ARG = 1, /* null pointer, overlap, memory not on the current device,
+                                 non-finite scale, sink/d_sink mismatch */
     SMLA_ERR_SHAPE = 2,       /* a size outside the limits above */
     SMLA_ERR_ALIGN = 3,       /* a pointer not aligned as required */
     SMLA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than the query function says */

@@ -142,10 +142,10 @@ def smla_fwd(q, kv, idx, sink=None, scale=None, out=None):
     T, H, _ = q.shape
     N, K = kv.shape[0], idx.shape[1]
     _need(q, "q", torch.bfloat16, (T, H, D))
-    _need(kv, "kv", torch.bfloat16, (N, D))
-    _need(idx, "idx", torch.int32, (T, K))
+    _need(kv, "kv", torch.bfloat16, (N, D), q.device)
+    _need(idx, "idx", torch.int32, (T, K), q.device)
     if sink is not None:
-        _need(sink, "sink", torch.float32, (H,))
+        _need(sink, "sink", torch.float32, (H,), q.device)
     if out is None:
         o = torch.empty_like(q)
         lse = torch.empty((T, H), dtype=torch.float32, device=q.device)
@@ -312,9 +312,9 @@ def smla_delta(o, dO, delta=None, dlse=None):
     """delta = rowsum(o * dO) (minus dlse when given), fp32 [T, H]."""
     T, H, _ = o.shape
     _need(o, "o", torch.bfloat16, (T, H, D))
-    _need(dO, "dO", torch.bfloat16, (T, H, D))
+    _need(dO, "dO", torch.bfloat16, (T, H, D), o.device)
     if dlse is not None:
-        _need(dlse, "dlse", torch.float32, (T, H))
+        _need(dlse, "dlse", torch.float32, (T, H), o.device)
     if delta is None:
         delta = torch.empty((T, H), dtype=torch.float32, device=o.device)
     else:
@@ -338,7 +338,7 @@ def smla_dq(q, kv, dO, lse, delta, idx, scale=None, dsp=None, dq=None):
     for t, n, dt, sh in ((q, "q", torch.bfloat16, (T, H, D)), (kv, "kv", torch.bfloat16, (N, D)),
                          (dO, "dO", torch.bfloat16, (T, H, D)), (lse, "lse", torch.float32, (T, H)),
                          (delta, "delta", torch.float32, (T, H)), (idx, "idx", torch.int32, (T, K))):
-        _need(t, n, dt, sh)
+        _need(t, n, dt, sh, q.device)
     if dq is None:
         dq = torch.empty_like(q)
     else:
@@ -357,9 +357,9 @@ def smla_interm(q, dO, dsp, idx, num_kv, interm=None):
     T, H, _ = q.shape
     K = idx.shape[1]
     _need(q, "q", torch.bfloat16, (T, H, D))
-    _need(dO, "dO", torch.bfloat16, (T, H, D))
-    _need(dsp, "dsp", torch.bfloat16, (dsp_numel(T, H, K),))
-    _need(idx, "idx", torch.int32, (T, K))
+    _need(dO, "dO", torch.bfloat16, (T, H, D), q.device)
+    _need(dsp, "dsp", torch.bfloat16, (dsp_numel(T, H, K),), q.device)
+    _need(idx, "idx", torch.int32, (T, K), q.device)
     if interm is None:
         interm = torch.empty((T * K, D), dtype=torch.bfloat16, device=q.device)
     else:

@@ -153,6 +153,38 @@ bool outputs_disjoint(const Range* all, int nall, int first_out) {
     return true;
 }
 
+// Every argument range must lie in device (or managed) memory of the current
+// device: a host pointer, or another device's buffer, reaching a kernel would
+// fault the GPU.  The first and the last byte of each range are looked up
+// (about 0.1 us each, no stream work, so also legal under graph capture); a
+// buffer that ends before its range does is caught as well whenever the bytes
+// past its end are not this device's memory.
+smla_status device_ranges(const Range* all, int nall) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SMLA_ERR_HIP;
+    for (int i = 0; i < nall; ++i) {
+        if (all[i].p == nullptr || all[i].n == 0) continue;
+        const char* first = static_cast<const char*>(all[i].p);
+        const char* ends[2] = {first, first + (all[i].n - 1)};
+        for (const char* p : ends) {
+            hipPointerAttribute_t a{};
+            if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+                (void)hipGetLastError();   // leave no error behind for the caller's next call
+                return SMLA_ERR_INVALID_ARG;
+            }
+            if ((a.type != hipMemoryTypeDevice && a.type != hipMemoryTypeManaged) || a.device != dev)
+                return SMLA_ERR_INVALID_ARG;
+        }
+    }
+    return SMLA_OK;
+}
+
+// Outputs disjoint from everything else, and every range on this device.
+smla_status check_ranges(const Range* all, int nall, int first_out) {
+    if (!outputs_disjoint(all, nall, first_out)) return SMLA_ERR_INVALID_ARG;
+    return device_ranges(all, nall);
+}
+
 smla_status check_shape(int T, int H, int num_kv, int topk) {
     if (T < 0 || H < 16 || H > 128 || H % 16 != 0 || topk < 1) return SMLA_ERR_SHAPE;
     if (num_kv < 1 || num_kv < T || num_kv >= (1 << 20)) return SMLA_ERR_SHAPE;
@@ -314,7 +346,7 @@ int smla_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const fl
     const size_t qb = (size_t)T * H * kD * 2;
     const Range all[] = {{q, qb}, {kv, (size_t)num_kv * kD * 2}, {idx, (size_t)T * topk * 4},
                          {sink, sink ? (size_t)H * 4 : 0}, {o, qb}, {lse, (size_t)T * H * 4}};
-    if (!outputs_disjoint(all, 6, 4)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 6, 4)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_fwd(q, kv, idx, sink, T, H, num_kv, topk, scale, o, lse,
                                  static_cast<hipStream_t>(stream)));
@@ -358,7 +390,7 @@ int bwd_impl(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const ui
                          {d_sink, d_sink ? hb : 0},
                          {n_invalid, n_invalid ? 4u : 0u},
                          {workspace, L.total}};
-    if (!outputs_disjoint(all, 13, 8)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 13, 8)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -533,7 +565,7 @@ int phased_impl(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const
                          {d_sink, d_sink ? hb : 0},
                          {n_invalid, n_invalid ? 4u : 0u},
                          {workspace, L.total}};
-    if (!outputs_disjoint(all, 13, 8)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 13, 8)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     if (use_scratch && (st = scratch_of_current_device(&workspace)) != SMLA_OK) return st;
 
@@ -642,7 +674,7 @@ int smla_delta(const uint16_t* o, const uint16_t* dO, const float* dlse, int T, 
     const size_t qb = (size_t)T * H * kD * 2;
     const size_t rb = (size_t)T * H * 4;
     const Range all[] = {{o, qb}, {dO, qb}, {dlse, dlse ? rb : 0}, {delta, rb}};
-    if (!outputs_disjoint(all, 4, 3)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 4, 3)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(
         launch_delta(o, dO, dlse, (int64_t)T * H, delta, static_cast<hipStream_t>(stream)));
@@ -664,7 +696,7 @@ int smla_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const flo
                          {dO, qb},         {lse, (size_t)T * H * 4},
                          {delta, (size_t)T * H * 4}, {idx, (size_t)T * topk * 4},
                          {dq, qb},         {dsp, dsp_bytes(T, H, topk)}};
-    if (!outputs_disjoint(all, 8, 6)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 8, 6)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_dq(q, kv, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dsp,
                                 static_cast<hipStream_t>(stream)));
@@ -684,7 +716,7 @@ int smla_interm(const uint16_t* q, const uint16_t* dO, const uint16_t* dsp, cons
                          {dsp, dsp_bytes(T, H, topk)},
                          {idx, (size_t)T * topk * 4},
                          {interm, (size_t)T * topk * kD * 2}};
-    if (!outputs_disjoint(all, 5, 4)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 5, 4)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm,
                                     static_cast<hipStream_t>(stream)));
@@ -707,7 +739,7 @@ int smla_build_csr(const int32_t* idx, int T, int topk, int num_kv, int32_t* row
                          {slots, (size_t)M * 4},
                          {n_invalid, n_invalid ? 4u : 0u},
                          {workspace, need}};
-    if (!outputs_disjoint(all, 5, 1)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 5, 1)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_csr(idx, M, num_kv, csr_carve(workspace, M, num_kv), row_ptr, slots,
                                  n_invalid, static_cast<hipStream_t>(stream)));
@@ -731,7 +763,7 @@ int smla_gather(const uint16_t* interm, const int32_t* row_ptr, const int32_t* s
                          {slots, 4},
                          {dkv, (size_t)num_kv * kD * 2},
                          {workspace, need}};
-    if (!outputs_disjoint(all, 5, 3)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 5, 3)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_gather(interm, row_ptr, slots, M, num_kv,
                                     gather_carve(workspace, M, num_kv), dkv,
@@ -753,7 +785,7 @@ int smla_dsink(const float* lse, const float* delta, const float* sink, int T, i
                          {sink, (size_t)H * 4},
                          {d_sink, (size_t)H * 4},
                          {workspace, need}};
-    if (!outputs_disjoint(all, 5, 3)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 5, 3)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_dsink(lse, delta, sink, T, H, static_cast<float*>(workspace), d_sink,
                                    static_cast<hipStream_t>(stream)));
@@ -786,7 +818,7 @@ int smla_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, con
                          {sink, sink ? (size_t)H * 4 : 0},
                          {o, qb},
                          {lse, (size_t)T * H * 4}};
-    if (!outputs_disjoint(all, 8, 6)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 8, 6)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
     return hip_status(launch_fwd_pe(q, q_pe, kv, k_pe, idx, sink, T, H, num_kv, topk, scale, o, lse,
                                     static_cast<hipStream_t>(stream)));
@@ -831,7 +863,7 @@ int smla_bwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, con
                          {d_sink, d_sink ? hb : 0},
                          {n_invalid, n_invalid ? 4u : 0u},
                          {workspace, L.total}};
-    if (!outputs_disjoint(all, 17, 10)) return SMLA_ERR_INVALID_ARG;
+    if ((st = check_ranges(all, 17, 10)) != SMLA_OK) return st;
     if ((st = check_arch()) != SMLA_OK) return st;
 
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -858,6 +858,42 @@ def test_error_codes_from_device_side_entry():
     assert e.value.status == 1   # dq aliases q
 
 
+def test_c_abi_refuses_memory_not_on_the_device():
+    """Host memory (pageable or pinned) handed to the C entry points in place of
+    an input, an output or the workspace is refused with SMLA_ERR_INVALID_ARG
+    before anything is enqueued (the device outputs keep their sentinel)."""
+    x = _to_dev(_oracle_inputs(_custom(8, 16, 8, 16, seed=2)))
+    T, H, _ = x["q"].shape
+    N, K = x["kv"].shape[0], x["idx"].shape[1]
+    lib, p = B.lib(), B._ptr
+    s = B._stream(x["q"].device)
+    host_q = torch.zeros_like(x["q"], device="cpu")
+    pinned = torch.zeros((T, H, 512), dtype=torch.bfloat16).pin_memory()
+    o = torch.full_like(x["q"], 7.0)
+    lse = torch.full((T, H), 7.0, device="cuda")
+    assert lib.smla_fwd(p(host_q), p(x["kv"]), p(x["idx"]), p(x["sink"]), T, H, N, K, SCALE, p(o), p(lse), s) == 1
+    assert lib.smla_fwd(p(x["q"]), p(x["kv"]), p(x["idx"]), p(x["sink"]), T, H, N, K, SCALE, p(pinned), p(lse),
+                        s) == 1
+    nbytes = B.bwd_workspace_bytes(T, H, N, K)
+    ws_dev = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    ws_host = torch.empty(nbytes, dtype=torch.uint8).pin_memory()
+    dq = torch.full_like(x["q"], 7.0)
+    dkv = torch.full_like(x["kv"], 7.0)
+    ds = torch.full((H,), 7.0, device="cuda")
+
+    def bwd(dq_ptr, ws):
+        return lib.smla_bwd(p(x["q"]), p(x["kv"]), p(x["dO"]), p(x["O"]), p(x["lse"]), p(x["idx"]), p(x["sink"]),
+                            None, T, H, N, K, SCALE, 0, dq_ptr, p(dkv), p(ds), None, p(ws), nbytes, s)
+
+    assert bwd(p(pinned), ws_dev) == 1
+    assert bwd(p(dq), ws_host) == 1
+    torch.cuda.synchronize()
+    assert torch.all(o.float() == 7.0) and torch.all(dq.float() == 7.0) and torch.all(dkv.float() == 7.0)
+    assert bwd(p(dq), ws_dev) == 0                      # the same call on device memory runs
+    torch.cuda.synchronize()
+    assert not torch.all(dq.float() == 7.0)
+
+
 # ---------------------------------------------------------------------------
 # token-phased backward (bounded workspace)
 # ---------------------------------------------------------------------------
