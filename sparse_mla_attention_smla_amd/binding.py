@@ -7,7 +7,10 @@ missing, every call raises.
 
 Function names follow the C entry points: smla_fwd, smla_bwd, smla_bwd_phased,
 smla_bwd_noalloc, smla_delta, smla_dq, smla_interm, smla_build_csr, smla_gather,
-smla_dsink, and the has_pe=True variant smla_fwd_pe, smla_bwd_pe.
+smla_dsink, and the has_pe=True variant smla_fwd_pe, smla_bwd_pe.  Above them:
+sparse_mla_bwd_dsv4 (the backward under the page's call form) and sparse_mla /
+SparseMLA (a torch.autograd.Function whose forward is smla_fwd and whose
+backward is smla_bwd).
 """
 from __future__ import annotations
 
@@ -497,3 +500,42 @@ def smla_bwd_pe(q, q_pe, kv, k_pe, dO, o, lse, idx, sink=None, scale=None, works
         _ptr(d_sink), _ptr(n_inv), _ptr(workspace), ws_bytes, _stream(dv)))
     res = (dq, dq_pe, dkv, dk_pe, d_sink)
     return res + (n_inv,) if count_invalid else res
+
+
+# ---------------------------------------------------------------------------
+# the page's call form, and autograd (argument marshalling only)
+# ---------------------------------------------------------------------------
+
+def sparse_mla_bwd_dsv4(q, kv, do, o, lse, topk, attn_sink=None, scale=None):
+    """The backward under the page's call form (same argument order, `topk` the
+    [T, topk] int32 index tensor, `attn_sink` the optional per-head sink):
+    returns (dq, dkv, d_sink), d_sink None without a sink."""
+    return smla_bwd(q, kv, do, o, lse, topk, attn_sink, scale)
+
+
+class SparseMLA(torch.autograd.Function):
+    """o, lse = smla_fwd(q, kv, idx, sink); its backward is smla_bwd, with the
+    gradient of lse (when lse is used) passed on as dlse.  Gradients flow to q,
+    kv and sink; idx takes none."""
+
+    @staticmethod
+    def forward(ctx, q, kv, idx, sink, scale):
+        o, lse = smla_fwd(q, kv, idx, sink, scale)
+        ctx.save_for_backward(q, kv, idx, o, lse, *(() if sink is None else (sink,)))
+        ctx.has_sink = sink is not None
+        ctx.scale = scale
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, dlse):
+        q, kv, idx, o, lse, *rest = ctx.saved_tensors
+        sink = rest[0] if ctx.has_sink else None
+        do = torch.zeros_like(o) if do is None else do.to(torch.bfloat16).contiguous()
+        dlse = None if dlse is None else dlse.to(torch.float32).contiguous()
+        dq, dkv, d_sink = smla_bwd(q, kv, do, o, lse, idx, sink, ctx.scale, dlse=dlse)
+        return dq, dkv, None, d_sink, None
+
+
+def sparse_mla(q, kv, idx, sink=None, scale=None):
+    """Differentiable sparse MLA attention: (o bf16 [T,H,512], lse fp32 [T,H])."""
+    return SparseMLA.apply(q, kv, idx, sink, scale)

@@ -894,6 +894,48 @@ def test_c_abi_refuses_memory_not_on_the_device():
     assert not torch.all(dq.float() == 7.0)
 
 
+def test_autograd_function_and_the_pages_call_form():
+    """sparse_mla under torch autograd (forward smla_fwd, backward smla_bwd): the
+    loss <O, W> + <lse, V> gives q.grad, kv.grad and sink.grad matching the oracle
+    backward with dO = W and dlse = V (on the O and lse the forward returned);
+    with only O used the gradients are smla_bwd's without dlse, bit for bit;
+    sparse_mla_bwd_dsv4 is smla_bwd."""
+    T, H, N, K = 37, 64, 60, 48
+    x = _custom(T, H, N, K, seed=12, sink=True, pool_frac=0.5)
+    x["idx"][4] = -1
+    W = inputs.normal_bf16((T, H, 512), 99, 7)
+    V = np.random.default_rng(5).standard_normal((T, H)).astype(np.float32)
+    idx = dev(x["idx"])
+
+    def leaves():
+        return (dev_bf16(x["q"]).requires_grad_(), dev_bf16(x["kv"]).requires_grad_(),
+                dev(x["sink"]).requires_grad_())
+
+    q, kv, sink = leaves()
+    o, lse = B.sparse_mla(q, kv, idx, sink)
+    ((o.float() * dev_bf16(W).float()).sum() + (lse * dev(V)).sum()).backward()
+    torch.cuda.synchronize()
+    # the backward's own inputs are the forward's outputs: the oracle backward
+    # takes those same O and lse (the forward is checked against the oracle too)
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    assert_close("O", host_bf16(o.detach()), O64)
+    ref = orc.backward(x["q"], x["kv"], W, host_bits(o.detach()), lse.detach().cpu().numpy(), x["idx"],
+                       x["sink"], SCALE, dlse=V)
+    assert_close("q.grad", host_bf16(q.grad), ref["dq"])
+    assert_close("kv.grad", host_bf16(kv.grad), ref["dkv"])
+    assert_close("sink.grad", sink.grad.cpu().numpy(), ref["d_sink"])
+    # only O in the loss: lse's gradient is zero, so the call is smla_bwd without dlse
+    q2, kv2, sink2 = leaves()
+    o2, lse2 = B.sparse_mla(q2, kv2, idx, sink2)
+    (o2.float() * dev_bf16(W).float()).sum().backward()
+    want = B.smla_bwd(q2.detach(), kv2.detach(), dev_bf16(W), o2.detach(), lse2.detach(), idx, sink2.detach())
+    page = B.sparse_mla_bwd_dsv4(q2.detach(), kv2.detach(), dev_bf16(W), o2.detach(), lse2.detach(), idx,
+                                 attn_sink=sink2.detach())
+    torch.cuda.synchronize()
+    for got, w, pg in ((q2.grad, want[0], page[0]), (kv2.grad, want[1], page[1]), (sink2.grad, want[2], page[2])):
+        assert torch.equal(got, w) and torch.equal(pg, w)
+
+
 # ---------------------------------------------------------------------------
 # token-phased backward (bounded workspace)
 # ---------------------------------------------------------------------------
