@@ -8,9 +8,10 @@ missing, every call raises.
 Function names follow the C entry points: smla_fwd, smla_bwd, smla_bwd_phased,
 smla_bwd_noalloc, smla_delta, smla_dq, smla_interm, smla_build_csr, smla_gather,
 smla_dsink, and the has_pe=True variant smla_fwd_pe, smla_bwd_pe.  Above them:
-sparse_mla_bwd_dsv4 (the backward under the page's call form) and sparse_mla /
+sparse_mla_bwd_dsv4 (the backward under the page's call form), sparse_mla /
 SparseMLA (a torch.autograd.Function whose forward is smla_fwd and whose
-backward is smla_bwd).
+backward is smla_bwd) and sparse_mla_pe / SparseMLAPE (the same over
+smla_fwd_pe / smla_bwd_pe).
 """
 from __future__ import annotations
 
@@ -539,3 +540,31 @@ class SparseMLA(torch.autograd.Function):
 def sparse_mla(q, kv, idx, sink=None, scale=None):
     """Differentiable sparse MLA attention: (o bf16 [T,H,512], lse fp32 [T,H])."""
     return SparseMLA.apply(q, kv, idx, sink, scale)
+
+
+class SparseMLAPE(torch.autograd.Function):
+    """The has_pe=True variant under autograd: o, lse = smla_fwd_pe(q, q_pe, kv,
+    k_pe, idx, sink); its backward is smla_bwd_pe, lse's gradient going in as
+    dlse.  Gradients flow to q, q_pe, kv, k_pe and sink."""
+
+    @staticmethod
+    def forward(ctx, q, q_pe, kv, k_pe, idx, sink, scale):
+        o, lse = smla_fwd_pe(q, q_pe, kv, k_pe, idx, sink, scale)
+        ctx.save_for_backward(q, q_pe, kv, k_pe, idx, o, lse, *(() if sink is None else (sink,)))
+        ctx.has_sink = sink is not None
+        ctx.scale = scale
+        return o, lse
+
+    @staticmethod
+    def backward(ctx, do, dlse):
+        q, q_pe, kv, k_pe, idx, o, lse, *rest = ctx.saved_tensors
+        sink = rest[0] if ctx.has_sink else None
+        do = torch.zeros_like(o) if do is None else do.to(torch.bfloat16).contiguous()
+        dlse = None if dlse is None else dlse.to(torch.float32).contiguous()
+        dq, dq_pe, dkv, dk_pe, d_sink = smla_bwd_pe(q, q_pe, kv, k_pe, do, o, lse, idx, sink, ctx.scale, dlse=dlse)
+        return dq, dq_pe, dkv, dk_pe, None, d_sink, None
+
+
+def sparse_mla_pe(q, q_pe, kv, k_pe, idx, sink=None, scale=None):
+    """Differentiable has_pe=True sparse MLA attention: (o, lse)."""
+    return SparseMLAPE.apply(q, q_pe, kv, k_pe, idx, sink, scale)

@@ -216,6 +216,34 @@ def test_pe_single_slot_tokens_cancel(H):
     assert got[4] is None
 
 
+def test_pe_autograd_function():
+    """sparse_mla_pe under torch autograd: the loss <O, W> + <lse, V> gives the
+    gradients of q, q_pe, kv, k_pe and sink matching the oracle backward with
+    dO = W and dlse = V, on the O and lse the forward returned."""
+    from tests._helpers import host_bits
+    T, H, N, K = 29, 64, 50, 40
+    rng = np.random.default_rng(17)
+    idx = rng.integers(0, N, size=(T, K)).astype(np.int32)
+    idx = np.where(rng.random((T, K)) < 0.3, -1, idx).astype(np.int32)
+    s = 7100
+    x = {"q": inputs.normal_bf16((T, H, 512), s, 1), "kv": inputs.normal_bf16((N, 512), s, 2),
+         "q_pe": inputs.normal_bf16((T, H, 64), s, 5), "k_pe": inputs.normal_bf16((N, 64), s, 6),
+         "idx": idx, "sink": rng.standard_normal(H).astype(np.float32)}
+    W = inputs.normal_bf16((T, H, 512), s, 7)
+    V = rng.standard_normal((T, H)).astype(np.float32)
+    q, q_pe, kv, k_pe = (dev_bf16(x[k]).requires_grad_() for k in ("q", "q_pe", "kv", "k_pe"))
+    sink = dev(x["sink"]).requires_grad_()
+    o, lse = B.sparse_mla_pe(q, q_pe, kv, k_pe, dev(idx), sink, SCALE_PE)
+    ((o.float() * dev_bf16(W).float()).sum() + (lse * dev(V)).sum()).backward()
+    torch.cuda.synchronize()
+    ref = orc.backward(x["q"], x["kv"], W, host_bits(o.detach()), lse.detach().cpu().numpy(), idx, x["sink"],
+                       SCALE_PE, dlse=V, q_pe=x["q_pe"], k_pe=x["k_pe"])
+    for name, g in (("dq", q.grad), ("dq_pe", q_pe.grad), ("dkv", kv.grad), ("dk_pe", k_pe.grad)):
+        rl, _, worst = assert_close(f"autograd {name}", host_bf16(g), ref[name])
+        _say(f"[pe autograd] {name}: rel-L2 {rl:.2e} worst row {worst:.2e}")
+    assert_close("autograd d_sink", sink.grad.cpu().numpy(), ref["d_sink"])
+
+
 def test_pe_zero_positional_parts_equal_the_plain_backward():
     """q_pe = 0: every logit is the plain one, so smla_bwd_pe must give smla_bwd's
     dq, dkv and d_sink (the plain call may take another dQ kernel, so up to
