@@ -692,6 +692,32 @@ def test_very_large_topk(H):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("scale,H", [(0.07, 64), (1.0 / 16, 16), (0.02, 128)])
+def test_non_default_scale(scale, H):
+    """Any finite scale, not only 1/sqrt(512): forward and backward against the
+    oracle at the same scale, with dlse (so every use of the scale is exercised:
+    the logits, dS, the dq and dkv terms and the lse)."""
+    T, N, K = 21, 40, 70
+    x = _custom(T, H, N, K, seed=int(scale * 1000) + H, sink=True, pool_frac=0.5)
+    x["idx"][5] = -1
+    _say(f"[scale] {scale} H={H}")
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], scale)
+    x["O"], x["lse"] = orc.emit_forward_outputs(O64, lse64)
+    d = _to_dev(x)
+    o, lse = B.smla_fwd(d["q"], d["kv"], d["idx"], d["sink"], scale)
+    dlse = np.random.default_rng(H).standard_normal((T, H)).astype(np.float32)
+    dq, dkv, ds = B.smla_bwd(d["q"], d["kv"], d["dO"], d["O"], d["lse"], d["idx"], d["sink"], scale,
+                             dlse=dev(dlse))
+    torch.cuda.synchronize()
+    assert_close("O", host_bf16(o), O64)
+    fin = np.isfinite(lse64)
+    assert np.max(np.abs(lse.cpu().numpy().astype(np.float64)[fin] - lse64[fin])) < 1e-4
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], scale, dlse=dlse)
+    assert_close("dq", host_bf16(dq), ref["dq"])
+    assert_close("dkv", host_bf16(dkv), ref["dkv"])
+    assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
+
+
 def _fuzz_case(seed):
     """A random small problem: any H the library takes, topk up to two index chunks,
     slots drawn with replacement (duplicate rows within a token), -1 padding and a
