@@ -692,13 +692,14 @@ def test_very_large_topk(H):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("scale,H", [(0.07, 64), (1.0 / 16, 16), (0.02, 128)])
+@pytest.mark.parametrize("scale,H", [(0.07, 64), (1.0 / 16, 16), (0.02, 128), (2.0, 64)])
 def test_non_default_scale(scale, H):
     """Any finite scale, not only 1/sqrt(512): forward and backward against the
     oracle at the same scale, with dlse (so every use of the scale is exercised:
-    the logits, dS, the dq and dkv terms and the lse)."""
+    the logits, dS, the dq and dkv terms and the lse); scale 2 gives logits of
+    about +-90, a nearly one-hot softmax."""
     T, N, K = 21, 40, 70
-    x = _custom(T, H, N, K, seed=int(scale * 1000) + H, sink=True, pool_frac=0.5)
+    x = _custom(T, H, N, K, seed=int(scale * 1000) % 997 + H, sink=True, pool_frac=0.5)
     x["idx"][5] = -1
     _say(f"[scale] {scale} H={H}")
     O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], scale)
