@@ -719,6 +719,29 @@ def test_non_default_scale(scale, H):
     assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
 
 
+def test_extreme_sink_values():
+    """Sinks of +30 (the sink takes nearly all the probability: P of about e^-30,
+    dq and the dS terms tiny but still relative-accurate), -30 (no effect) and
+    0 across the heads: forward, backward and d_sink against the oracle, per head."""
+    T, H, N, K = 19, 64, 30, 40
+    x = _custom(T, H, N, K, seed=4321, sink=True, pool_frac=0.5)
+    x["sink"] = np.tile(np.array([30.0, -30.0, 0.0, 12.0], dtype=np.float32), H // 4)
+    x = _oracle_inputs(x)
+    d = _to_dev(x)
+    o, lse = B.smla_fwd(d["q"], d["kv"], d["idx"], d["sink"], SCALE)
+    dq, dkv, ds = _run_bwd(d)
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    assert np.max(np.abs(lse.cpu().numpy().astype(np.float64) - lse64)) < 1e-4
+    ref = orc.backward(x["q"], x["kv"], x["dO"], x["O"], x["lse"], x["idx"], x["sink"], SCALE)
+    got_o, got_dq = host_bf16(o), host_bf16(dq)
+    for h0 in range(4):   # each sink value on its own: the +30 heads are ~e^-30 smaller
+        sl = slice(h0, None, 4)
+        assert_close(f"O (sink {x['sink'][h0]})", got_o[:, sl], O64[:, sl])
+        assert_close(f"dq (sink {x['sink'][h0]})", got_dq[:, sl], ref["dq"][:, sl])
+        assert_close(f"d_sink (sink {x['sink'][h0]})", ds.cpu().numpy()[sl], ref["d_sink"][sl])
+    assert_close("dkv", host_bf16(dkv), ref["dkv"])
+
+
 def _fuzz_case(seed):
     """A random small problem: any H the library takes, topk up to two index chunks,
     slots drawn with replacement (duplicate rows within a token), -1 padding and a
