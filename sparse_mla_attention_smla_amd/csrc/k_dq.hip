@@ -4,10 +4,11 @@
 // row: the gathered kv rows are read from LDS once and feed both the S and dP
 // products; the kernel also writes this pass's dS and P.
 //
-// Work unit: one query token t and a group of NW*16 heads (one wave = 16
-// heads).  Per wave, q and dO of its heads stay in registers as MFMA B
-// operands for the whole token.  The token's valid slots are compacted and
-// walked in tiles of 32 kv rows copied straight into a 4-deep LDS ring:
+// Work unit: one query token t and a group of 64 heads (the last group of a
+// token padded when H is not a multiple of 64), walked by persistent
+// workgroups of producer and consumer waves (below).  The token's valid slots
+// are compacted and streamed in tiles of 32 kv rows copied straight into an
+// LDS ring:
 //   S^T, dP^T [32 slots x 16 heads] = kv_tile . {q, dO}^T     (MFMA, reduce d=512)
 //   P  = exp(scale*S - lse)
 //   dS = P * (dP - delta)
@@ -15,8 +16,8 @@
 // The S^T accumulator leaves each lane with one head and 8 slots, which is
 // exactly the B-operand layout of the second product: no data exchange.
 //
-// The persistent variant below also runs the forward (smla_k7_fwd_pc): the same
-// stream and roles, with an online softmax in place of the gradient.
+// The same stream and roles also run the forward (smla_k7_fwd_pc), with an
+// online softmax in place of the gradient.
 //
 // dsp layout (consumed by the intermediate kernel): for token t and compacted
 // tile c (c < ceil(topk/32)), a block of 2H x 32 bf16 values at
@@ -30,201 +31,6 @@
 #include "smla_launch.hpp"
 
 namespace smla {
-
-// PE adds the has_pe=True variant's positional part: q_pe [T,H,64] (B operands
-// of two more S^T steps), k_pe [N,64] (a second, 4 KiB tile ring, see
-// kv_tile.hpp), and dq_pe [T,H,64] = scale * sum_k dS k_pe, accumulated from
-// the same dS fragment as dq.
-template <int NW, bool PE>
-__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(1, 1)))
-void smla_k2_dq(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
-                const uint16_t* __restrict__ dO, const float* __restrict__ lse,
-                const float* __restrict__ delta, const int32_t* __restrict__ idx, int H,
-                int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp,
-                const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe,
-                uint16_t* __restrict__ dq_pe) {
-    static_assert(kNBuf == 4, "the vmcnt bounds below assume a 4-deep ring");
-    constexpr int R = kBK / NW + (PE ? 4 / NW : 0);   // buffer->LDS copies per wave per tile
-    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
-    __shared__ __attribute__((aligned(16))) char pe_tiles[PE ? kNBuf * kPeTileBytes : 16];
-    __shared__ SlotList L;
-
-    const int nhg = H / (NW * 16);
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int t = logical / nhg;
-    const int hg = logical - t * nhg;
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index (uniform)
-    const int lane = threadIdx.x & 63, c16 = lane & 15, g = lane >> 4;
-    const int h = hg * NW * 16 + w * 16 + c16;
-    const size_t qrow = ((size_t)t * H + h) * kD;
-    const int32_t* idx_row = idx + (size_t)t * K;
-    if (w == 0) compact_slots(idx_row, K, N, 0, &L, lane);
-
-    u32x4 qf[16], dof[16];
-#pragma unroll
-    for (int ds = 0; ds < 16; ++ds) {
-        qf[ds] = *reinterpret_cast<const u32x4*>(q + qrow + 32 * ds + 8 * g);
-        dof[ds] = *reinterpret_cast<const u32x4*>(dO + qrow + 32 * ds + 8 * g);
-    }
-    u32x4 qpf[2];
-    const size_t prow = ((size_t)t * H + h) * kDP;
-    if constexpr (PE) {
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) qpf[s2] = *reinterpret_cast<const u32x4*>(q_pe + prow + 32 * s2 + 8 * g);
-    }
-    const float lse_h = lse[(size_t)t * H + h];
-    const float bias = (lse_h == -INFINITY) ? INFINITY : lse_h * kLog2e;
-    const float c = scale * kLog2e;
-    const float dl = delta[(size_t)t * H + h];
-    const i32x4 rsrc = make_rsrc(kv, (uint32_t)N * (kD * 2));
-    const i32x4 rsrc_pe = make_rsrc(k_pe, PE ? (uint32_t)N * kPeRow : 0u);
-    const uint32_t ring = lds_addr(tiles);
-    const uint32_t pe_ring = lds_addr(pe_tiles);
-    const int rb = rows_base(c16, g), cb = cols_base(c16, g);
-    const int ntk = (K + kBK - 1) / kBK;
-    uint16_t* dsp_tok = dsp + (size_t)t * ntk * (2 * H) * kBK;
-
-    f32x4 acc[32], acc_pe[4];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc_pe[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto issue = [&](int ct) {
-        issue_tile<NW>(rsrc, &L, ct, ring + (ct % kNBuf) * kTileBytes, w, lane);
-        if constexpr (PE) issue_pe_tile<NW>(rsrc_pe, &L, ct, pe_ring + (ct % kNBuf) * kPeTileBytes, w, lane);
-    };
-    // the positional part of S^T for tile slot `slot` of the ring
-    auto s_pe = [&](f32x4 (&sacc)[2], int slot) {
-        if constexpr (PE) {
-            const char* pbuf = pe_tiles + slot * kPeTileBytes;
-#pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-                for (int st = 0; st < 2; ++st) sacc[st] = mfma16(pe_rows_a(pbuf, c16, g, st, s2), qpf[s2], sacc[st]);
-        }
-    };
-    auto dq_pe_step = [&](int slot, u32x4 bf) {
-        if constexpr (PE) {
-            const char* pbuf = pe_tiles + slot * kPeTileBytes;
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) acc_pe[dt] = mfma16(pe_cols_a(pbuf, c16, g, dt), bf, acc_pe[dt]);
-        }
-    };
-
-    // Software pipeline over the compacted tiles of a chunk.  Iteration j
-    // turns tile j's S/dP accumulators into P and dS (VALU, stores), then runs
-    // one unrolled block that interleaves the dq MFMAs of tile j with the S/dP
-    // MFMAs of tile j+1: two independent MFMA chains hide each other's LDS read
-    // latency.  Tile j+3 is copied into the ring slot tile j-1 used.
-    // VMEM ops per wave: R copies per tile and the dS/P stores; the vmcnt bound
-    // when waiting for tile j+1 counts only the copies issued after its own.
-    int ctg = 0;  // compacted tiles of earlier chunks
-    for (int k0 = 0; k0 < K; k0 += kChunk) {
-        if (k0 > 0 && w == 0) compact_slots(idx_row, K, N, k0, &L, lane);
-        __syncthreads();
-        const int n = L.n;
-        const int ntile = (n + kBK - 1) / kBK;
-#pragma unroll
-        for (int p = 0; p < kNBuf - 1; ++p) issue(p);
-        if (ntile > 0) {
-            f32x4 sacc[2], pacc[2];
-            wait_vmcnt<(2 * R < 63 ? 2 * R : 63)>();
-            __syncthreads();
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int ds = 0; ds < 16; ++ds) {
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    const u32x4 a = tile_rows_a(tiles, rb, st, ds);
-                    sacc[st] = mfma16(a, qf[ds], sacc[st]);
-                    pacc[st] = mfma16(a, dof[ds], pacc[st]);
-                }
-            }
-            s_pe(sacc, 0);
-            // P and scale*dS of tile j from its accumulators; stores; B operand of dq
-            auto softmax_grad = [&](int j) -> u32x4 {
-                float dss[2][4], ps[2][4];
-#pragma unroll
-                for (int st = 0; st < 2; ++st)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const bool v = j * kBK + 16 * st + 4 * g + i < n;
-                        const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[st][i], c, -bias)) : 0.f;
-                        ps[st][i] = p;
-                        dss[st][i] = p * (pacc[st][i] - dl) * scale;
-                    }
-                // one 16-byte piece per lane and kind (dsp piece layout): the
-                // lanes of a wave write 1 KiB contiguously
-                uint16_t* blk = dsp_tok + (size_t)(ctg + j) * (2 * H) * kBK + (size_t)(h - c16) * kBK + lane * 8;
-                const u32x4 dsv = {pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
-                                   pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
-                *reinterpret_cast<u32x4*>(blk) = dsv;
-                *reinterpret_cast<u32x4*>(blk + (size_t)H * kBK) =
-                    u32x4{pack_bf16(ps[0][0], ps[0][1]), pack_bf16(ps[0][2], ps[0][3]),
-                          pack_bf16(ps[1][0], ps[1][1]), pack_bf16(ps[1][2], ps[1][3])};
-                return dsv;
-            };
-            for (int j = 0; j + 1 < ntile; ++j) {
-                // Only the copies of tile j+2 are younger loads than those of tile
-                // j+1.  The dS/P stores in between are not counted: a store may
-                // retire before an older load, so an allowance for stores could
-                // let the wait pass early.  Over-waiting on them is safe.
-                wait_vmcnt<(R < 63 ? R : 63)>();
-                __syncthreads();  // tile j+1 landed everywhere; ring slot of tile j-1 is free
-                issue(j + kNBuf - 1);
-                const u32x4 bf = softmax_grad(j);
-                const char* bufa = tiles + (j % kNBuf) * kTileBytes;
-                const char* bufb = tiles + ((j + 1) % kNBuf) * kTileBytes;
-#pragma unroll
-                for (int st = 0; st < 2; ++st) {
-                    sacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    pacc[st] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-#pragma unroll
-                for (int ds = 0; ds < 16; ++ds) {
-                    acc[2 * ds] = mfma16(tile_cols_a(bufa, cb, 2 * ds), bf, acc[2 * ds]);
-                    acc[2 * ds + 1] = mfma16(tile_cols_a(bufa, cb, 2 * ds + 1), bf, acc[2 * ds + 1]);
-#pragma unroll
-                    for (int st = 0; st < 2; ++st) {
-                        const u32x4 a = tile_rows_a(bufb, rb, st, ds);
-                        sacc[st] = mfma16(a, qf[ds], sacc[st]);
-                        pacc[st] = mfma16(a, dof[ds], pacc[st]);
-                    }
-                }
-                dq_pe_step(j % kNBuf, bf);
-                s_pe(sacc, (j + 1) % kNBuf);
-            }
-            const int jl = ntile - 1;
-            const u32x4 bf = softmax_grad(jl);
-            const char* bufl = tiles + (jl % kNBuf) * kTileBytes;
-#pragma unroll
-            for (int dt = 0; dt < 32; ++dt) acc[dt] = mfma16(tile_cols_a(bufl, cb, dt), bf, acc[dt]);
-            dq_pe_step(jl % kNBuf, bf);
-        }
-        ctg += ntile;
-        wait_vmcnt<0>();   // the ring's trailing copies land before LDS is reused
-        __syncthreads();
-    }
-
-    // lane holds dq^T rows d = 16*dt + 4g .. +3 of head h: 4 contiguous bf16
-#pragma unroll
-    for (int dt = 0; dt < 32; ++dt) {
-        const u32x2 v = {pack_bf16(acc[dt][0], acc[dt][1]), pack_bf16(acc[dt][2], acc[dt][3])};
-        *reinterpret_cast<u32x2*>(dq + qrow + 16 * dt + 4 * g) = v;
-    }
-    if constexpr (PE) {
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-            const u32x2 v = {pack_bf16(acc_pe[dt][0], acc_pe[dt][1]), pack_bf16(acc_pe[dt][2], acc_pe[dt][3])};
-            *reinterpret_cast<u32x2*>(dq_pe + prow + 16 * dt + 4 * g) = v;
-        }
-    }
-}
 
 // Items of one persistent workgroup: ids lo + r * G below n_items, r < count.
 // The items are dealt in rounds of G consecutive ids.  With a grid that is a
@@ -247,9 +53,10 @@ struct ItemSeq {
     __device__ int item(int r) const { return lo + r * step; }
 };
 
-// Persistent producer/consumer variant for 64-head groups (H % 64 == 0): one
-// 512-thread workgroup per CU walks its items (token, 64 heads); an item is cut
-// into segments of up to 512 index slots.  Waves w and w+4 share a SIMD
+// Persistent producer/consumer kernels over 64-head groups: one 512-thread
+// workgroup per CU walks its items (token, 64 heads; when H is not a multiple
+// of 64, the last group of each token is padded, see PAD below); an item is
+// cut into segments of up to 512 index slots.  Waves w and w+4 share a SIMD
 // (measured on gfx950 from HW_ID), so each SIMD runs one wave of each role:
 //   producers (waves 0-3): 16 heads each, q and dO in registers; per tile the
 //     S^T, dP^T products, then P and scale*dS (stored as dsp blocks) and the dS
@@ -330,7 +137,7 @@ __device__ __forceinline__ void settle_scalars(float a, float b) {
 // its 64 columns each).  The ring is then 3 tiles deep instead of 4 so that
 // both rings fit in LDS: the stream only ever holds the consumers' tile, the
 // producers' tile and the one being copied.
-template <bool PROD, bool FWD, bool PE = false>
+template <bool PROD, bool FWD, bool PE = false, bool PAD = false>
 __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                            const uint16_t* __restrict__ dO, const float* __restrict__ lse,
                                            const float* __restrict__ delta, const int32_t* __restrict__ idx,
@@ -350,7 +157,10 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     constexpr int kWarmTiles = 8;   // tiles over which the next item's q/dO are warmed (32 chunks)
     const int c16 = lane & 15, g = lane >> 4;
     auto ring_slot = [](int pos) { return NB == 4 ? (pos & 3) : pos % NB; };
-    const int nhg = H / 64;
+    // PAD: H a multiple of 16 but not of 64; the last group of each token holds
+    // H % 64 heads, and the producers whose 16 heads lie past H run on head H-1
+    // and store nothing
+    const int nhg = PAD ? (H + 63) / 64 : H / 64;
     const ItemSeq seq(blockIdx.x, gridDim.x, T * nhg);
     const int spi = (K + kChunk - 1) / kChunk;   // segments per item
     const int nseg = seq.count() * spi;
@@ -380,15 +190,24 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     auto item_rows = [&](int item, int& h, size_t& lrow) {
         const int t = item / nhg, hg = item - t * nhg;
         h = hg * 64 + w * 16 + c16;
+        if constexpr (PAD) h = h < H ? h : H - 1;
         lrow = (size_t)t * H + h;
     };
+    // PAD: whether this producer's 16 heads of `item` exist (wave-uniform)
+    auto wave_active = [&](int item) { return (item % nhg) * 64 + w * 16 < H; };
+    bool p_act = true;              // PAD: of the item being produced
     auto bias_of = [](float l) { return (l == -INFINITY) ? INFINITY : l * kLog2e; };
     auto sink_of = [&](int h) { return sink != nullptr ? sink[h] * kLog2e : -INFINITY; };
     // first element of this lane's load row (lane 4*c16 + g: head c16, chunk g)
     auto frag_src = [&](int item) {
         const int t = item / nhg, hg = item - t * nhg;
-        return ((size_t)t * H + hg * 64 + w * 16 + frag_load_lane_row(lane)) * kD +
-               8 * frag_load_lane_chunk(lane);
+        if constexpr (PAD) {
+            const int hrow = hg * 64 + w * 16 + frag_load_lane_row(lane);
+            return ((size_t)t * H + (hrow < H ? hrow : H - 1)) * kD + 8 * frag_load_lane_chunk(lane);
+        } else {
+            return ((size_t)t * H + hg * 64 + w * 16 + frag_load_lane_row(lane)) * kD +
+                   8 * frag_load_lane_chunk(lane);
+        }
     };
     // PE: first element of this lane's q_pe fragment (loaded in MFMA order: 2 loads)
     auto pe_src = [&](int item) {
@@ -442,7 +261,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             osc = a / z;
             lse_v = (m_fin + log2f(z)) * kLn2;
         }
-        if (g == 0) lse_out[p_item_row + c16] = lse_v;
+        if (g == 0 && (!PAD || p_act)) lse_out[p_item_row + c16] = lse_v;
         m_use = -INFINITY;
         l_run = 0.f;
         return osc;
@@ -452,6 +271,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         const int item = seg_item(s);
         size_t lrow;
         item_rows(item, p_h, lrow);
+        if constexpr (PAD) p_act = wave_active(item);
         if (new_item) { bias = nbias; dl = ndl; p_ctg = 0; }
         p_n = Lb[s & 1].n;
         if constexpr (FWD) {
@@ -575,10 +395,12 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             uint16_t* blk = p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK + (size_t)(p_h - c16) * kBK + lane * 8;
             const u32x4 dsv = {pack_bf16(dss[0][0], dss[0][1]), pack_bf16(dss[0][2], dss[0][3]),
                                pack_bf16(dss[1][0], dss[1][1]), pack_bf16(dss[1][2], dss[1][3])};
-            *reinterpret_cast<u32x4*>(blk) = dsv;
-            *reinterpret_cast<u32x4*>(blk + (size_t)H * kBK) =
-                u32x4{pack_bf16(ps[0][0], ps[0][1]), pack_bf16(ps[0][2], ps[0][3]),
-                      pack_bf16(ps[1][0], ps[1][1]), pack_bf16(ps[1][2], ps[1][3])};
+            if (!PAD || p_act) {
+                *reinterpret_cast<u32x4*>(blk) = dsv;
+                *reinterpret_cast<u32x4*>(blk + (size_t)H * kBK) =
+                    u32x4{pack_bf16(ps[0][0], ps[0][1]), pack_bf16(ps[0][2], ps[0][3]),
+                          pack_bf16(ps[1][0], ps[1][1]), pack_bf16(ps[1][2], ps[1][3])};
+            }
             sh.dsfrag[pos & 1][w][lane] = dsv;
         }
     };
@@ -616,7 +438,9 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         const int it = real ? item_next : 0;
         const int t = it / nhg, hg = it - t * nhg;
         const uint16_t* rows = (k < 16 ? q : dO) + ((size_t)t * H + hg * 64) * kD;
-        copy_row_to_lds(make_rsrc(rows, real ? 65536u : 0u), touch_lds, (k & 15) * 4096 + lane * 64);
+        // PAD: a short last group reads only its own heads (past them: nothing)
+        const uint32_t span = PAD ? (uint32_t)min(64, H - hg * 64) * (kD * 2) : 65536u;
+        copy_row_to_lds(make_rsrc(rows, real ? span : 0u), touch_lds, (k & 15) * 4096 + lane * 64);
     };
     auto consume = [&](int pos) {
         const int cb = cols_base(c16, g);
@@ -667,8 +491,21 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     // with the item's last tile at position pos_last (-1: the item has no tile).
     auto epilogue = [&](int item, int pos_last) {
         const int t = item / nhg, hg = item - t * nhg;
+        // PAD: the stores go through buffer ranges that end at the group's last
+        // head, so those of heads past H are dropped by the hardware; they are
+        // still issued, which keeps the vmcnt bounds above exact
+        __amdgpu_buffer_rsrc_t out_rsrc, pe_rsrc;
+        if constexpr (PAD) {
+            const int nh = min(64, H - hg * 64);
+            out_rsrc = __builtin_amdgcn_make_buffer_rsrc(dq + ((size_t)t * H + hg * 64) * kD, (short)0,
+                                                         nh * kD * 2, 0x00020000);
+            if constexpr (PE && !FWD)
+                pe_rsrc = __builtin_amdgcn_make_buffer_rsrc(dq_pe + ((size_t)t * H + hg * 64) * kDP, (short)0,
+                                                            nh * kDP * 2, 0x00020000);
+        }
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
+            const int hl = 16 * m + (lane >> 2);   // PAD: head within the group
             const int h = hg * 64 + 16 * m + (lane >> 2);
             uint16_t* out = dq + ((size_t)t * H + h) * kD + 128 * dq4 + 4 * (lane & 3);
             float sc = 0.f;
@@ -677,16 +514,26 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             for (int dt = 0; dt < 8; ++dt) {
                 f32x4 v = acc[dt][m];
                 if constexpr (FWD) v *= sc;
-                *reinterpret_cast<u32x2*>(out + 16 * dt) =
-                    to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane);
+                if constexpr (PAD)
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane), out_rsrc,
+                        (hl * kD + 128 * dq4 + 4 * (lane & 3) + 16 * dt) * 2, 0, 0);
+                else
+                    *reinterpret_cast<u32x2*>(out + 16 * dt) =
+                        to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane);
                 acc[dt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
             if constexpr (PE && !FWD) {
                 // dq_pe^T rows 16dq4 + 4g .. +3 of head 16m + c16, stored quad-contiguous
                 uint16_t* op = dq_pe + ((size_t)t * H + h) * kDP + 16 * dq4 + 4 * (lane & 3);
                 const f32x4 v = acc_pe[m];
-                *reinterpret_cast<u32x2*>(op) =
-                    to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane);
+                if constexpr (PAD)
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane), pe_rsrc,
+                        (hl * kDP + 16 * dq4 + 4 * (lane & 3)) * 2, 0, 0);
+                else
+                    *reinterpret_cast<u32x2*>(op) =
+                        to_quad_rows(u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])}, lane);
                 acc_pe[m] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
         }
@@ -911,59 +758,143 @@ void smla_k7_fwd_pc_pe(const uint16_t* __restrict__ q, const uint16_t* __restric
                                       lane, sink, lse, q_pe, k_pe, nullptr);
 }
 
-hipError_t launch_fwd_pc(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
-                         int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
-                         hipStream_t s) {
-    const int items = T * (H / 64);
+// The four persistent kernels for head counts that are a multiple of 16 but
+// not of 64 (the last group of each token padded to 64 heads, see PAD above):
+// the same streams, the same LDS.
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k2_dq_pcx(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                    const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                    const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
+                    int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
+    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    const DqShared sh{tiles, Lb, dsfrag, touch, nullptr, nullptr, nullptr};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4) dq_pc_role<true, false, false, true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
+    else dq_pc_role<false, false, false, true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k7_fwd_pcx(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                     const int32_t* __restrict__ idx, const float* __restrict__ sink, int T, int H,
+                     int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    __shared__ __attribute__((aligned(16))) int resc[2][4];
+    __shared__ float alpha[2][4][16];
+    __shared__ float oscale[2][4][16];
+    const DqShared sh{tiles, Lb, dsfrag, touch, resc, alpha, oscale};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, true, false, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh,
+                                            w, lane, sink, lse);
+    else
+        dq_pc_role<false, true, false, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh,
+                                             w, lane, sink, lse);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k2_dq_pcx_pe(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                       const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                       const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
+                       int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp,
+                       const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe,
+                       uint16_t* __restrict__ dq_pe) {
+    __shared__ __attribute__((aligned(16))) char tiles[3 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char pe_tiles[3 * kPeTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    const DqShared sh{tiles, Lb, dsfrag, touch, nullptr, nullptr, nullptr, pe_tiles};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, false, true, true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane,
+                                            nullptr, nullptr, q_pe, k_pe, dq_pe);
+    else
+        dq_pc_role<false, false, true, true>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane,
+                                             nullptr, nullptr, q_pe, k_pe, dq_pe);
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k7_fwd_pcx_pe(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                        const int32_t* __restrict__ idx, const float* __restrict__ sink, int T, int H,
+                        int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse,
+                        const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe) {
+    __shared__ __attribute__((aligned(16))) char tiles[3 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char pe_tiles[3 * kPeTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    __shared__ __attribute__((aligned(16))) int resc[2][4];
+    __shared__ float alpha[2][4][16];
+    __shared__ float oscale[2][4][16];
+    const DqShared sh{tiles, Lb, dsfrag, touch, resc, alpha, oscale, pe_tiles};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, true, true, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh, w,
+                                           lane, sink, lse, q_pe, k_pe, nullptr);
+    else
+        dq_pc_role<false, true, true, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh, w,
+                                            lane, sink, lse, q_pe, k_pe, nullptr);
+}
+
+// Persistent grid: one workgroup per compute unit (its LDS use admits one),
+// never more than there are items (token, 64-head group).
+static hipError_t persistent_blocks(int T, int H, unsigned* blocks) {
+    const int items = T * ((H + 63) / 64);
     int cus = 0;
     const hipError_t e = compute_units(&cus);
     if (e != hipSuccess) return e;
-    const unsigned blocks = (unsigned)(items < cus ? items : cus);
-    smla_k7_fwd_pc<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse);
+    *blocks = (unsigned)(items < cus ? items : cus);
+    return hipSuccess;
+}
+
+hipError_t launch_fwd_pc(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
+                         int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
+                         hipStream_t s) {
+    unsigned blocks = 0;
+    const hipError_t e = persistent_blocks(T, H, &blocks);
+    if (e != hipSuccess) return e;
+    if (H % 64 == 0)
+        smla_k7_fwd_pc<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse);
+    else
+        smla_k7_fwd_pcx<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse);
     return hipGetLastError();
 }
 
-// Heads per workgroup: 64, 32 or 16 (whichever divides H first).
-int dq_waves(int H) {
-    if (H % 64 == 0) return 4;
-    if (H % 32 == 0) return 2;
-    return 1;
-}
 
 hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, const float* lse,
                      const float* delta, const int32_t* idx, int T, int H, int N, int K, float scale,
                      uint16_t* dq, uint16_t* dsp, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    const int nw = dq_waves(H);
-    if (nw == 4) {
-        // persistent: one workgroup per compute unit (its LDS use admits one)
-        const int items = T * (H / 64);
-        int cus = 0;
-        const hipError_t e = compute_units(&cus);
-        if (e != hipSuccess) return e;
-        const unsigned blocks = (unsigned)(items < cus ? items : cus);
+    unsigned blocks = 0;
+    const hipError_t e = persistent_blocks(T, H, &blocks);
+    if (e != hipSuccess) return e;
+    if (H % 64 == 0)
         smla_k2_dq_pc<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
-        return hipGetLastError();
-    }
-    const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
-    if (nw == 2)
-        smla_k2_dq<2, false><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
-                                                    nullptr, nullptr, nullptr);
     else
-        smla_k2_dq<1, false><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
-                                                   nullptr, nullptr, nullptr);
+        smla_k2_dq_pcx<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
     return hipGetLastError();
 }
 
 hipError_t launch_fwd_pc_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
                             const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
                             uint16_t* o, float* lse, hipStream_t s) {
-    const int items = T * (H / 64);
-    int cus = 0;
-    const hipError_t e = compute_units(&cus);
+    unsigned blocks = 0;
+    const hipError_t e = persistent_blocks(T, H, &blocks);
     if (e != hipSuccess) return e;
-    const unsigned blocks = (unsigned)(items < cus ? items : cus);
-    smla_k7_fwd_pc_pe<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe);
+    if (H % 64 == 0)
+        smla_k7_fwd_pc_pe<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe);
+    else
+        smla_k7_fwd_pcx_pe<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe);
     return hipGetLastError();
 }
 
@@ -972,33 +903,15 @@ hipError_t launch_dq_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t*
                         int H, int N, int K, float scale, uint16_t* dq, uint16_t* dq_pe, uint16_t* dsp,
                         hipStream_t s) {
     if (T == 0) return hipSuccess;
-    const int nw = dq_waves(H);
-    if (nw == 4) {
-        // persistent, as for the plain op
-        const int items = T * (H / 64);
-        int cus = 0;
-        const hipError_t e = compute_units(&cus);
-        if (e != hipSuccess) return e;
-        const unsigned blocks = (unsigned)(items < cus ? items : cus);
+    unsigned blocks = 0;
+    const hipError_t e = persistent_blocks(T, H, &blocks);
+    if (e != hipSuccess) return e;
+    if (H % 64 == 0)
         smla_k2_dq_pc_pe<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, q_pe,
                                                 k_pe, dq_pe);
-        return hipGetLastError();
-    }
-    const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
-    switch (nw) {
-        case 4:
-            smla_k2_dq<4, true><<<blocks, 256, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
-                                                       q_pe, k_pe, dq_pe);
-            break;
-        case 2:
-            smla_k2_dq<2, true><<<blocks, 128, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
-                                                       q_pe, k_pe, dq_pe);
-            break;
-        default:
-            smla_k2_dq<1, true><<<blocks, 64, 0, s>>>(q, kv, dO, lse, delta, idx, H, N, K, scale, dq, dsp,
-                                                      q_pe, k_pe, dq_pe);
-            break;
-    }
+    else
+        smla_k2_dq_pcx_pe<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, q_pe,
+                                                 k_pe, dq_pe);
     return hipGetLastError();
 }
 

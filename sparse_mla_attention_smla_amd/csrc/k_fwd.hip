@@ -158,7 +158,14 @@ void smla_k7_fwd(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv
     if (g == 0) lse[(size_t)t * H + h] = lse_v;
 }
 
-int dq_waves(int H);
+// Heads per workgroup of the one-wave-per-16-heads forward: 64, 32 or 16
+// (whichever divides H first).
+static int dq_waves(int H) {
+    if (H % 64 == 0) return 4;
+    if (H % 32 == 0) return 2;
+    return 1;
+}
+
 hipError_t launch_fwd_pc(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
                          int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
                          hipStream_t s);
@@ -167,9 +174,10 @@ hipError_t launch_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx,
                       int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
                       hipStream_t s) {
     if (T == 0) return hipSuccess;
-    // 64-head groups with one index chunk per token: the persistent kernel
-    // (k_dq.hip) that shares the dQ pass's tile stream and wave roles
-    if (H % 64 == 0 && K <= kChunk) return launch_fwd_pc(q, kv, idx, sink, T, H, N, K, scale, o, lse, s);
+    // one index chunk per token: the persistent kernel (k_dq.hip) that shares
+    // the dQ pass's tile stream and wave roles (64-head groups, the last one
+    // padded when H is not a multiple of 64)
+    if (K <= kChunk) return launch_fwd_pc(q, kv, idx, sink, T, H, N, K, scale, o, lse, s);
     const int nw = dq_waves(H);
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
     switch (nw) {
@@ -188,7 +196,7 @@ hipError_t launch_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t
                          const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
                          uint16_t* o, float* lse, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (H % 64 == 0 && K <= kChunk) return launch_fwd_pc_pe(q, q_pe, kv, k_pe, idx, sink, T, H, N, K, scale, o, lse, s);
+    if (K <= kChunk) return launch_fwd_pc_pe(q, q_pe, kv, k_pe, idx, sink, T, H, N, K, scale, o, lse, s);
     const int nw = dq_waves(H);
     const unsigned blocks = (unsigned)T * (unsigned)(H / (nw * 16));
     switch (nw) {

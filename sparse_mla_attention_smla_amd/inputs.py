@@ -86,6 +86,11 @@ WORKLOADS = {
     # (pool of stride 1, so late tokens see up to 320 pool rows)
     "mid": Workload("mid", 6, T=320, H=128, num_kv=640, topk=512,
                     selection="swa_pool", window=128, pool_stride=1, pool_picks=384),
+    # the headline's tokens and index recipe at the head counts of a head-sharded
+    # model (and H = 48, 96: groups of 64 heads with a partial last one)
+    **{f"headline_h{h}": Workload(f"headline_h{h}", 30 + h // 16, T=4096, H=h, num_kv=5120, topk=512,
+                                  selection="swa_pool", window=128, pool_stride=4, pool_picks=384)
+       for h in (16, 32, 48, 96)},
 }
 
 
