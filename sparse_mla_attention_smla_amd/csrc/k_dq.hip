@@ -137,7 +137,7 @@ __device__ __forceinline__ void settle_scalars(float a, float b) {
 // its 64 columns each).  The ring is then 3 tiles deep instead of 4 so that
 // both rings fit in LDS: the stream only ever holds the consumers' tile, the
 // producers' tile and the one being copied.
-template <bool PROD, bool FWD, bool PE = false, bool PAD = false>
+template <bool PROD, bool FWD, bool PE = false, bool PAD = false, int SPLIT = 0>
 __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                            const uint16_t* __restrict__ dO, const float* __restrict__ lse,
                                            const float* __restrict__ delta, const int32_t* __restrict__ idx,
@@ -187,14 +187,26 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     size_t p_item_row = 0;          // forward: row of lse_out of the wave's first head
     uint16_t* p_blk = dsp;          // dsp block of the item's compacted tile 0
     const float c = scale * kLog2e;
+    // PAD: the 16-head blocks of an item's group (1 to 4).  SPLIT (backward,
+    // H = 16 * SPLIT, one group of one or two blocks per token): each block gets
+    // two producers, each taking one 16-slot half of every tile (the backward's
+    // softmax needs no reduction over slots), so all four SIMDs share the work.
+    static_assert(SPLIT == 0 || (PAD && !FWD && SPLIT <= 2), "split groups: backward, 16 or 32 heads");
+    auto blocks_of = [&](int item) { return min(4, (H - (item % nhg) * 64) >> 4); };
+    // the producer's head block of `item` (SPLIT: w / 2)
+    auto head_block = [&](int item) { return SPLIT > 0 ? (w >> 1) : w; };
     auto item_rows = [&](int item, int& h, size_t& lrow) {
         const int t = item / nhg, hg = item - t * nhg;
-        h = hg * 64 + w * 16 + c16;
-        if constexpr (PAD) h = h < H ? h : H - 1;
+        if constexpr (PAD) {
+            h = hg * 64 + head_block(item) * 16 + c16;
+            h = h < H ? h : H - 1;
+        } else {
+            h = hg * 64 + w * 16 + c16;
+        }
         lrow = (size_t)t * H + h;
     };
     // PAD: whether this producer's 16 heads of `item` exist (wave-uniform)
-    auto wave_active = [&](int item) { return (item % nhg) * 64 + w * 16 < H; };
+    auto wave_active = [&](int item) { return head_block(item) < blocks_of(item); };
     bool p_act = true;              // PAD: of the item being produced
     auto bias_of = [](float l) { return (l == -INFINITY) ? INFINITY : l * kLog2e; };
     auto sink_of = [&](int h) { return sink != nullptr ? sink[h] * kLog2e : -INFINITY; };
@@ -202,7 +214,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     auto frag_src = [&](int item) {
         const int t = item / nhg, hg = item - t * nhg;
         if constexpr (PAD) {
-            const int hrow = hg * 64 + w * 16 + frag_load_lane_row(lane);
+            const int hrow = hg * 64 + head_block(item) * 16 + frag_load_lane_row(lane);
             return ((size_t)t * H + (hrow < H ? hrow : H - 1)) * kD + 8 * frag_load_lane_chunk(lane);
         } else {
             return ((size_t)t * H + hg * 64 + w * 16 + frag_load_lane_row(lane)) * kD +
@@ -404,6 +416,64 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             sh.dsfrag[pos & 1][w][lane] = dsv;
         }
     };
+    // SPLIT: the 16-slot half st = w % 2 of tile jt for the
+    // block's 16 heads (the same steps as produce on one half); the dsp pieces and
+    // the dS fragment get this half's 8 bytes, the block's other producer the rest
+    auto produce_half = [&](int pos, int jt, auto reload, const uint16_t* nq, const uint16_t* nd,
+                            const uint16_t* nqp) {
+        const int st = w & 1;
+        const char* buf = sh.tiles + ring_slot(pos) * kTileBytes;
+        const int rb = rows_base(c16, g);
+        f32x4 sacc = {0.f, 0.f, 0.f, 0.f}, pacc = {0.f, 0.f, 0.f, 0.f};
+        constexpr int PF = 2;
+        u32x4 ab[16];
+#pragma unroll
+        for (int ds = 0; ds < PF; ++ds) ab[ds] = tile_rows_a(buf, rb, st, ds);
+        __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
+#pragma unroll
+        for (int ds = 0; ds < 16; ++ds) {
+            if (ds + PF < 16) ab[ds + PF] = tile_rows_a(buf, rb, st, ds + PF);
+            sacc = mfma16(ab[ds], qf[ds], sacc);
+            pacc = mfma16(ab[ds], dof[ds], pacc);
+            if (ds + PF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            if constexpr (decltype(reload)::value) {
+                qf[ds] = *reinterpret_cast<const u32x4*>(nq + 32 * ds);
+                dof[ds] = *reinterpret_cast<const u32x4*>(nd + 32 * ds);
+            }
+        }
+        if constexpr (PE) {
+            const char* pbuf = sh.pe_tiles + ring_slot(pos) * kPeTileBytes;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) sacc = mfma16(pe_rows_a(pbuf, c16, g, st, s2), qpf[s2], sacc);
+            if constexpr (decltype(reload)::value) {
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2) qpf[s2] = *reinterpret_cast<const u32x4*>(nqp + 32 * s2);
+            }
+        }
+        float dss[4], ps[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool v = jt * kBK + 16 * st + 4 * g + i < p_n;
+            const float p = v ? __builtin_amdgcn_exp2f(fmaf(sacc[i], c, -bias)) : 0.f;
+            ps[i] = p;
+            dss[i] = p * (pacc[i] - dl) * scale;
+        }
+        if (p_act) {
+            uint16_t* blk =
+                p_blk + (size_t)(p_ctg + jt) * (2 * H) * kBK + (size_t)(p_h - c16) * kBK + lane * 8 + 4 * st;
+            const u32x2 dsv = {pack_bf16(dss[0], dss[1]), pack_bf16(dss[2], dss[3])};
+            *reinterpret_cast<u32x2*>(blk) = dsv;
+            *reinterpret_cast<u32x2*>(blk + (size_t)H * kBK) = u32x2{pack_bf16(ps[0], ps[1]), pack_bf16(ps[2], ps[3])};
+            reinterpret_cast<u32x2*>(&sh.dsfrag[pos & 1][w >> 1][lane])[st] = dsv;
+        }
+    };
+    // the tile's producer work
+    auto produce_tile = [&](int pos, int jt, auto reload, const uint16_t* nq, const uint16_t* nd,
+                            const uint16_t* nqp) {
+        if constexpr (SPLIT > 0) produce_half(pos, jt, reload, nq, nd, nqp);
+        else produce(pos, jt, reload, nq, nd, nqp);
+    };
     using NoReload = std::integral_constant<bool, false>;
     using Reload = std::integral_constant<bool, true>;
 
@@ -484,6 +554,55 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
 #pragma unroll
             for (int m = 0; m < 4; ++m) acc_pe[m] = mfma16(pa, b[m], acc_pe[m]);
         }
+    };
+    // SPLIT: only the group's head blocks are multiplied
+    auto consume_nb = [&](int pos, auto nb_c) {
+        constexpr int NBK = decltype(nb_c)::value;   // head blocks of the item
+        const int cb = cols_base(c16, g);
+        u32x4 b[4];
+#pragma unroll
+        for (int m = 0; m < NBK; ++m) b[m] = sh.dsfrag[pos & 1][m][lane];
+        const char* buf = sh.tiles + ring_slot(pos) * kTileBytes;
+        // transposed kv reads two d-blocks ahead of their four MFMAs (pinned)
+        u32x4 ca[8];
+        ca[0] = tile_cols_a(buf, cb, 8 * dq4);
+        ca[1] = tile_cols_a(buf, cb, 8 * dq4 + 1);
+        if constexpr (FWD) {
+            // lane c16 + 16g of acc[.][m] belongs to head 16m + c16: apply the
+            // producers' rescale factors before this tile's P is added.  The
+            // four flags are one 16-byte read issued with the operand reads
+            // above, so the check adds no LDS round trip of its own (reading
+            // them first and branching per flag cost the forward 9%).
+            const u32x4 rf = *reinterpret_cast<const u32x4*>(sh.resc[pos & 1]);
+            if (__builtin_amdgcn_readfirstlane(rf[0] | rf[1] | rf[2] | rf[3])) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if (__builtin_amdgcn_readfirstlane(rf[m])) {
+                        const float a = sh.alpha[pos & 1][m][c16];
+#pragma unroll
+                        for (int dt = 0; dt < 8; ++dt) acc[dt][m] *= a;
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, NBK + 4, 0);
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            if (dt + 2 < 8) ca[dt + 2] = tile_cols_a(buf, cb, 8 * dq4 + dt + 2);
+#pragma unroll
+            for (int m = 0; m < NBK; ++m) acc[dt][m] = mfma16(ca[dt], b[m], acc[dt][m]);
+            if (dt + 2 < 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NBK, 0);
+        }
+        if constexpr (PE && !FWD) {
+            const u32x4 pa = pe_cols_a(sh.pe_tiles + ring_slot(pos) * kPeTileBytes, c16, g, dq4);
+#pragma unroll
+            for (int m = 0; m < NBK; ++m) acc_pe[m] = mfma16(pa, b[m], acc_pe[m]);
+        }
+    };
+    auto consume_any = [&](int pos) {
+        if constexpr (SPLIT > 0) consume_nb(pos, std::integral_constant<int, SPLIT>{});
+        else consume(pos);
     };
     // lane c16 + 16g holds dq^T rows d = 128dq4 + 16dt + 4g .. +3 of head 16m + c16;
     // stored quad-contiguous (lane 4*c + g writes head 16m + c)
@@ -576,7 +695,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             }
             __syncthreads();
             if constexpr (PROD) {
-                if (ntile > 0) produce(base, 0, NoReload{}, nullptr, nullptr, nullptr);
+                if (ntile > 0) produce_tile(base, 0, NoReload{}, nullptr, nullptr, nullptr);
             }
         }
         for (int j = 0; j < ntile; ++j) {
@@ -609,7 +728,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                         const int nitem = seg_item(s + 1);
                         item_rows(nitem, h, lrow);
                         const size_t src = frag_src(nitem);
-                        produce(pos + 1, j + 1, Reload{}, q + src, dO + src, PE ? q_pe + pe_src(nitem) : nullptr);
+                        produce_tile(pos + 1, j + 1, Reload{}, q + src, dO + src, PE ? q_pe + pe_src(nitem) : nullptr);
                         if constexpr (FWD) {
                             nbias = sink_of(h);
                         } else {
@@ -618,12 +737,12 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                         }
                         finish_load();
                     } else {
-                        produce(pos + 1, j + 1, NoReload{}, nullptr, nullptr, nullptr);
+                        produce_tile(pos + 1, j + 1, NoReload{}, nullptr, nullptr, nullptr);
                     }
                 } else if (cont) {
                     if (!next_new_item) p_ctg += ntile;
                     enter_segment(s + 1, next_new_item);
-                    if (p_n > 0) produce(pos + 1, 0, NoReload{}, nullptr, nullptr, nullptr);
+                    if (p_n > 0) produce_tile(pos + 1, 0, NoReload{}, nullptr, nullptr, nullptr);
                 }
             } else {
                 const int ahead = j + kAhead;
@@ -634,7 +753,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                     const bool warm = next_new_item && j >= first && j + 2 < ntile;
                     touch(warm ? seg_item(s + 1) : -1, (j - first) * 4 + dq4);
                 }
-                consume(pos);
+                consume_any(pos);
                 if (post_epi > 0) --post_epi;
                 ++since;
                 if (j + 1 == ntile && last_of_item) {
@@ -846,6 +965,53 @@ void smla_k7_fwd_pcx_pe(const uint16_t* __restrict__ q, const uint16_t* __restri
                                             lane, sink, lse, q_pe, k_pe, nullptr);
 }
 
+// Backward for 16 or 32 heads (SPLIT = H / 16): one group per token whose
+// head blocks each get two producers, one per 16-slot half of every tile.
+template <int SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k2_dq_pcs(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                    const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                    const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
+                    int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp) {
+    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    const DqShared sh{tiles, Lb, dsfrag, touch, nullptr, nullptr, nullptr};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, false, false, true, SPLIT>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh,
+                                                    w, lane);
+    else
+        dq_pc_role<false, false, false, true, SPLIT>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh,
+                                                     w, lane);
+}
+
+template <int SPLIT>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k2_dq_pcs_pe(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                       const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                       const float* __restrict__ delta, const int32_t* __restrict__ idx, int T, int H,
+                       int N, int K, float scale, uint16_t* __restrict__ dq, uint16_t* __restrict__ dsp,
+                       const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe,
+                       uint16_t* __restrict__ dq_pe) {
+    __shared__ __attribute__((aligned(16))) char tiles[3 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char pe_tiles[3 * kPeTileBytes];
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    const DqShared sh{tiles, Lb, dsfrag, touch, nullptr, nullptr, nullptr, pe_tiles};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, false, true, true, SPLIT>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w,
+                                                   lane, nullptr, nullptr, q_pe, k_pe, dq_pe);
+    else
+        dq_pc_role<false, false, true, true, SPLIT>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w,
+                                                    lane, nullptr, nullptr, q_pe, k_pe, dq_pe);
+}
+
 // Persistent grid: one workgroup per compute unit (its LDS use admits one),
 // never more than there are items (token, 64-head group).
 static hipError_t persistent_blocks(int T, int H, unsigned* blocks) {
@@ -880,6 +1046,10 @@ hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, 
     if (e != hipSuccess) return e;
     if (H % 64 == 0)
         smla_k2_dq_pc<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
+    else if (H == 16)
+        smla_k2_dq_pcs<1><<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
+    else if (H == 32)
+        smla_k2_dq_pcs<2><<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
     else
         smla_k2_dq_pcx<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp);
     return hipGetLastError();
@@ -909,6 +1079,12 @@ hipError_t launch_dq_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t*
     if (H % 64 == 0)
         smla_k2_dq_pc_pe<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, q_pe,
                                                 k_pe, dq_pe);
+    else if (H == 16)
+        smla_k2_dq_pcs_pe<1><<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, q_pe,
+                                                    k_pe, dq_pe);
+    else if (H == 32)
+        smla_k2_dq_pcs_pe<2><<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, q_pe,
+                                                    k_pe, dq_pe);
     else
         smla_k2_dq_pcx_pe<<<blocks, 512, 0, s>>>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, q_pe,
                                                  k_pe, dq_pe);
