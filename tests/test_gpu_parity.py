@@ -1115,6 +1115,12 @@ def _check_all_rows(name, x, ref, dq, dkv, ds):
 _OTHER_SHAPES = {
     "t16384_h16": inputs.Workload("t16384_h16", 22, T=16384, H=16, num_kv=20480, topk=512, selection="swa_pool",
                                   window=128, pool_stride=4, pool_picks=384),
+    # head counts that are not a multiple of 64, with several items per persistent
+    # workgroup: 32 heads (slot-split producers), 48 and 112 (a last group of three
+    # 16-head blocks), 80 (of one), 96 (of two)
+    **{f"t{T}_h{H}": inputs.Workload(f"t{T}_h{H}", 40 + H // 16, T=T, H=H, num_kv=T + T // 4, topk=512,
+                                     selection="swa_pool", window=128, pool_stride=4, pool_picks=384)
+       for T, H in ((1500, 32), (1200, 48), (600, 80), (700, 96), (600, 112))},
     "t3000": inputs.Workload("t3000", 20, T=3000, H=128, num_kv=3750, topk=512, selection="swa_pool",
                              window=128, pool_stride=4, pool_picks=384),
     "t2500_h64_k480": inputs.Workload("t2500_h64_k480", 21, T=2500, H=64, num_kv=3125, topk=480,

@@ -244,6 +244,29 @@ def test_pe_autograd_function():
     assert_close("autograd d_sink", sink.grad.cpu().numpy(), ref["d_sink"])
 
 
+@pytest.mark.parametrize("H", [32, 48])
+def test_pe_full_rows_other_head_counts(H):
+    """has_pe=True at 32 heads (slot-split producers) and 48 (a padded last
+    group), 700 tokens, so persistent workgroups stream across items: every row
+    of dq, dq_pe, dkv, dk_pe and d_sink, and the forward's O and lse."""
+    w = inputs.Workload(f"pe_h{H}", 60 + H // 16, T=700, H=H, num_kv=875, topk=512, selection="swa_pool",
+                        window=128, pool_stride=4, pool_picks=384)
+    x = dict(inputs.make(w, sink=True))
+    x["q_pe"], x["k_pe"] = inputs.make_pe(w)
+    x["scale"] = SCALE_PE
+    x = _with_forward(x)
+    _say(f"[pe rows] H={H}: T={w.T}")
+    d = _dev(x)
+    got = _bwd(d, x)
+    ref = oracle_backward_chunked(x)
+    _check(f"H={H} T={w.T}", x, ref, got)
+    o, lse = B.smla_fwd_pe(d["q"], d["q_pe"], d["kv"], d["k_pe"], d["idx"], d["sink"], x["scale"])
+    torch.cuda.synchronize()
+    assert_close("O", host_bf16(o), x["O64"])
+    fin = np.isfinite(x["lse"])
+    assert np.max(np.abs(lse.cpu().numpy().astype(np.float64)[fin] - x["lse"][fin].astype(np.float64))) < 1e-4
+
+
 def test_pe_zero_positional_parts_equal_the_plain_backward():
     """q_pe = 0: every logit is the plain one, so smla_bwd_pe must give smla_bwd's
     dq, dkv and d_sink (the plain call may take another dQ kernel, so up to
