@@ -41,7 +41,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="headline")
+    ap.add_argument("--workload", default="headline",
+                    help="a seeded workload of sparse_mla_attention_smla_amd/inputs.py: headline (the "
+                         "default and the metric's), skewed, long, mid, small, tiny, or headline_h16/"
+                         "h32/h48/h64/h96 (the headline's tokens and indices at other head counts)")
     ap.add_argument("--cpu-baseline", choices=["on", "off"], default="on")
     ap.add_argument("--phased", choices=["on", "off"], default="off",
                     help="also time the bounded-workspace backward (1024-token phases); its "
