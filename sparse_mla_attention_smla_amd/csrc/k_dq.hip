@@ -803,8 +803,8 @@ void smla_k2_dq_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ 
     else dq_pc_role<false, false>(q, kv, dO, lse, delta, idx, T, H, N, K, scale, dq, dsp, sh, w, lane);
 }
 
-// Forward on the same persistent stream (64-head groups, topk <= 512): o and
-// lse for every (token, head).
+// Forward on the same persistent stream (64-head groups with H % 64 == 0,
+// topk <= 512): o and lse for every (token, head).
 __global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
 void smla_k7_fwd_pc(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                     const int32_t* __restrict__ idx, const float* __restrict__ sink, int T, int H,

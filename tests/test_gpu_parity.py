@@ -497,10 +497,10 @@ def test_forward_matches_oracle(name, sink):
     (23, 128, 60, 33, False),   # two 64-head groups, 2 tiles per token, no sink
     (50, 64, 50, 1, True),      # topk = 1: every token has at most one tile
     (9, 64, 300, 96, True),     # most kv rows unused
-    (19, 32, 19, 16, True),     # one-wave-per-16-heads kernel, two waves per block
-    (21, 96, 45, 64, False),    # the same kernel with three head blocks, no sink
-    (25, 48, 33, 40, True),     # one wave per block
-    (12, 64, 80, 600, True),    # topk beyond one index chunk: four waves per block
+    (19, 32, 19, 16, True),     # 32 heads: a padded group of two 16-head blocks
+    (21, 96, 45, 64, False),    # 96 heads: a full group and a padded one, no sink
+    (25, 48, 33, 40, True),     # 48 heads: a padded group of three blocks
+    (12, 64, 80, 600, True),    # topk beyond one index chunk: the one-wave-per-16-heads kernel
 ])
 def test_forward_ragged(T, H, N, K, sink):
     x = _custom(T, H, N, K, seed=7 * T + H, sink=sink, pool_frac=0.5)

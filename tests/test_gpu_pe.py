@@ -125,8 +125,8 @@ def _custom_pe(T, H, N, K, seed, sink=True, dup=False):
 
 
 @pytest.mark.parametrize("T,H,N,K,sink,dup,with_dlse", [
-    (37, 48, 53, 40, True, False, False),    # one wave per 16 heads, ragged tail tile
-    (21, 32, 45, 64, False, True, True),     # two waves per block, duplicates / out of range, dlse
+    (37, 48, 53, 40, True, False, False),    # a padded 48-head group, ragged tail tile
+    (21, 32, 45, 64, False, True, True),     # slot-split 32 heads, duplicates / out of range, dlse
     (12, 64, 80, 600, True, True, False),    # topk beyond one index chunk
     (9, 128, 300, 96, True, False, True),    # most kv rows unused, dlse
     (17, 112, 30, 33, True, True, False),    # 7 head blocks of 16, 4 reduction steps with a half
