@@ -16,8 +16,10 @@
 // The S^T accumulator leaves each lane with one head and 8 slots, which is
 // exactly the B-operand layout of the second product: no data exchange.
 //
-// The same stream and roles also run the forward (smla_k7_fwd_pc), with an
-// online softmax in place of the gradient.
+// The same stream and roles also run the forward (smla_k7_fwd_pc*), with an
+// online softmax in place of the gradient.  Page, Contract section: the
+// forward's lse is sink-inclusive (the sink enters the running max and sum
+// once, before lse = max + ln(sum)) and the sink carries no value vector.
 //
 // dsp layout (consumed by the intermediate kernel): for token t and compacted
 // tile c (c < ceil(topk/32)), a block of 2H x 32 bf16 values at
@@ -88,6 +90,10 @@ struct DqShared {
     float (*alpha)[4][16];
     float (*oscale)[4][16];
     char* pe_tiles;     // has_pe=True: ring slots of kPeTileBytes (positional key rows)
+    // forward over several index chunks per item, [position parity][producer][lane]:
+    // the producer lane's running softmax state after that tile (reference max,
+    // its share of the sum); the consumers finish each head from it
+    float (*mst)[4][64][2] = nullptr;
 };
 
 constexpr int kMinStream = 5;  // segments this long hand over to the next without a drain
@@ -137,7 +143,7 @@ __device__ __forceinline__ void settle_scalars(float a, float b) {
 // its 64 columns each).  The ring is then 3 tiles deep instead of 4 so that
 // both rings fit in LDS: the stream only ever holds the consumers' tile, the
 // producers' tile and the one being copied.
-template <bool PROD, bool FWD, bool PE = false, bool PAD = false, int SPLIT = 0>
+template <bool PROD, bool FWD, bool PE = false, bool PAD = false, int SPLIT = 0, bool MULTI = false>
 __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
                                            const uint16_t* __restrict__ dO, const float* __restrict__ lse,
                                            const float* __restrict__ delta, const int32_t* __restrict__ idx,
@@ -152,8 +158,14 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     constexpr int kAhead = 2;                    // tiles copied ahead of the consumers
     static_assert(NB > kAhead, "the ring holds the consumers', the producers' and the copied tile");
     constexpr int R = kBK / 4 + (PE ? 1 : 0);    // copies per consumer wave per tile
-    // global stores of one consumer epilogue (4 heads x 8 d-blocks, + 4 of dq_pe)
-    constexpr int kEpiStores = 32 + (PE && !FWD ? 4 : 0);
+    // MULTI (forward, topk > 512): an item streams through several segments, so
+    // no tile is known to be its last when produced; the producers publish their
+    // softmax state every tile and the consumers finish each head (output scale,
+    // lse) in their epilogue, from the state of the item's last consumed tile
+    static_assert(!MULTI || FWD, "several segments per forward item");
+    // global stores of one consumer epilogue (4 heads x 8 d-blocks, + 4 of dq_pe,
+    // or + 4 of lse)
+    constexpr int kEpiStores = 32 + (PE && !FWD ? 4 : 0) + (MULTI ? 4 : 0);
     constexpr int kWarmTiles = 8;   // tiles over which the next item's q/dO are warmed (32 chunks)
     const int c16 = lane & 15, g = lane >> 4;
     auto ring_slot = [](int pos) { return NB == 4 ? (pos & 3) : pos % NB; };
@@ -288,7 +300,14 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         p_n = Lb[s & 1].n;
         if constexpr (FWD) {
             p_item_row = lrow - c16;
-            if (p_n == 0) (void)finish_softmax();   // no valid slot: only lse is written
+            if constexpr (MULTI) {
+                if (new_item) {
+                    m_use = -INFINITY;
+                    l_run = 0.f;
+                }
+            } else {
+                if (p_n == 0) (void)finish_softmax();   // no valid slot: only lse is written
+            }
         } else {
             p_blk = dsp + (size_t)(item / nhg) * ntk * (2 * H) * kBK;
         }
@@ -385,7 +404,9 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             sh.dsfrag[par][w][lane] =
                 u32x4{pack_bf16(ps[0][0], ps[0][1]), pack_bf16(ps[0][2], ps[0][3]),
                       pack_bf16(ps[1][0], ps[1][1]), pack_bf16(ps[1][2], ps[1][3])};
-            if (jt == (p_n + kBK - 1) / kBK - 1) {
+            if constexpr (MULTI) {
+                *reinterpret_cast<float2*>(sh.mst[par][w][lane]) = make_float2(m_use, l_run);
+            } else if (jt == (p_n + kBK - 1) / kBK - 1) {
                 const float osc = finish_softmax();
                 if (g == 0) sh.oscale[par][w][c16] = osc;
             }
@@ -613,7 +634,13 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         // PAD: the stores go through buffer ranges that end at the group's last
         // head, so those of heads past H are dropped by the hardware; they are
         // still issued, which keeps the vmcnt bounds above exact
-        __amdgpu_buffer_rsrc_t out_rsrc, pe_rsrc;
+        __amdgpu_buffer_rsrc_t out_rsrc, pe_rsrc, lse_rsrc;
+        if constexpr (MULTI) {
+            // the group's lse row; lanes that do not write it store past its end
+            const int nh = PAD ? min(64, H - hg * 64) : 64;
+            lse_rsrc = __builtin_amdgcn_make_buffer_rsrc(lse_out + (size_t)t * H + hg * 64, (short)0, nh * 4,
+                                                         0x00020000);
+        }
         if constexpr (PAD) {
             const int nh = min(64, H - hg * 64);
             out_rsrc = __builtin_amdgcn_make_buffer_rsrc(dq + ((size_t)t * H + hg * 64) * kD, (short)0,
@@ -628,7 +655,30 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
             const int h = hg * 64 + 16 * m + (lane >> 2);
             uint16_t* out = dq + ((size_t)t * H + h) * kD + 128 * dq4 + 4 * (lane & 3);
             float sc = 0.f;
-            if constexpr (FWD) sc = pos_last >= 0 ? sh.oscale[pos_last & 1][m][c16] : 0.f;
+            if constexpr (FWD && MULTI) {
+                // head 16m + c16 of the group: its softmax as the producers left it
+                // at the item's last tile (none: empty), with the sink folded in
+                float mu = -INFINITY, lt = 0.f;
+                if (pos_last >= 0) {
+                    const float (*st)[2] = sh.mst[pos_last & 1][m];
+                    mu = st[c16][0];
+                    lt = (st[c16][1] + st[c16 + 16][1]) + (st[c16 + 32][1] + st[c16 + 48][1]);
+                }
+                const int hh = hg * 64 + 16 * m + c16;
+                const float b = sink != nullptr ? sink[hh < H ? hh : H - 1] * kLog2e : -INFINITY;
+                const float m_fin = fmaxf(mu, b);
+                float lse_v = -INFINITY;
+                if (m_fin != -INFINITY) {
+                    const float a = __builtin_amdgcn_exp2f(mu - m_fin);
+                    const float z = lt * a + __builtin_amdgcn_exp2f(b - m_fin);
+                    sc = a / z;
+                    lse_v = (m_fin + log2f(z)) * kLn2;
+                }
+                __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), lse_rsrc,
+                                                      (dq4 == 0 && g == 0) ? (16 * m + c16) * 4 : 256, 0, 0);
+            } else if constexpr (FWD) {
+                sc = pos_last >= 0 ? sh.oscale[pos_last & 1][m][c16] : 0.f;
+            }
 #pragma unroll
             for (int dt = 0; dt < 8; ++dt) {
                 f32x4 v = acc[dt][m];
@@ -668,6 +718,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
     __syncthreads();
 
     SlotChunk nxt;     // producer 0: index slots of the next segment, loaded early
+    int c_last = -1;   // consumer: position of the current item's last consumed tile
     int base = 0;      // stream position of tile 0 of segment s
     bool primed = false;
     int post_epi = 0;  // consumer: iterations whose wait must skip the last epilogue's stores
@@ -681,6 +732,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
         const bool next_new_item = has_next && last_of_item;
         const bool cont = has_next && ntile >= kMinStream;
         const int item = seg_item(s);
+        if (first_of_item) c_last = -1;
         const int32_t* idx_next = has_next ? idx + (size_t)(seg_item(s + 1) / nhg) * K : idx;
         const int k0_next = has_next ? seg_k0(s + 1) : 0;
         if (!primed) {
@@ -754,6 +806,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                     touch(warm ? seg_item(s + 1) : -1, (j - first) * 4 + dq4);
                 }
                 consume_any(pos);
+                c_last = pos;
                 if (post_epi > 0) --post_epi;
                 ++since;
                 if (j + 1 == ntile && last_of_item) {
@@ -773,7 +826,7 @@ __device__ __forceinline__ void dq_pc_role(const uint16_t* __restrict__ q, const
                 }
             } else {
                 if (w == 4 && has_next && ntile < 2) compact_slots(idx_next, K, N, k0_next, &Lb[(s + 1) & 1], lane);
-                if (ntile == 0 && last_of_item) epilogue(item, -1);
+                if (ntile == 0 && last_of_item) epilogue(item, MULTI ? c_last : -1);
                 wait_vmcnt<0>();
                 post_epi = 0;
             }
@@ -1012,6 +1065,52 @@ void smla_k2_dq_pcs_pe(const uint16_t* __restrict__ q, const uint16_t* __restric
                                                     lane, nullptr, nullptr, q_pe, k_pe, dq_pe);
 }
 
+// Forward with topk above one index chunk (several segments per item, MULTI):
+// plain and has_pe, with 64-head groups or a padded last group.
+template <bool PE, bool PAD>
+__device__ __forceinline__ void fwd_pcm_body(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                                             const int32_t* __restrict__ idx, const float* __restrict__ sink,
+                                             int T, int H, int N, int K, float scale, uint16_t* __restrict__ o,
+                                             float* __restrict__ lse, const uint16_t* __restrict__ q_pe,
+                                             const uint16_t* __restrict__ k_pe, char* tiles, char* pe_tiles) {
+    __shared__ SlotList Lb[2];
+    __shared__ u32x4 dsfrag[2][4][64];
+    __shared__ __attribute__((aligned(16))) char touch[1024];
+    __shared__ __attribute__((aligned(16))) int resc[2][4];
+    __shared__ float alpha[2][4][16];
+    __shared__ float oscale[2][4][16];
+    __shared__ __attribute__((aligned(16))) float mst[2][4][64][2];
+    const DqShared sh{tiles, Lb, dsfrag, touch, resc, alpha, oscale, pe_tiles, mst};
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (w < 4)
+        dq_pc_role<true, true, PE, PAD, 0, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh,
+                                                 w, lane, sink, lse, q_pe, k_pe, nullptr);
+    else
+        dq_pc_role<false, true, PE, PAD, 0, true>(q, kv, q, nullptr, nullptr, idx, T, H, N, K, scale, o, nullptr, sh,
+                                                  w, lane, sink, lse, q_pe, k_pe, nullptr);
+}
+
+template <bool PAD>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k7_fwd_pcm(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                     const int32_t* __restrict__ idx, const float* __restrict__ sink, int T, int H,
+                     int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse) {
+    __shared__ __attribute__((aligned(16))) char tiles[kNBuf * kTileBytes];
+    fwd_pcm_body<false, PAD>(q, kv, idx, sink, T, H, N, K, scale, o, lse, nullptr, nullptr, tiles, nullptr);
+}
+
+template <bool PAD>
+__global__ __attribute__((amdgpu_flat_work_group_size(512, 512), amdgpu_waves_per_eu(2, 2)))
+void smla_k7_fwd_pcm_pe(const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv,
+                        const int32_t* __restrict__ idx, const float* __restrict__ sink, int T, int H,
+                        int N, int K, float scale, uint16_t* __restrict__ o, float* __restrict__ lse,
+                        const uint16_t* __restrict__ q_pe, const uint16_t* __restrict__ k_pe) {
+    __shared__ __attribute__((aligned(16))) char tiles[3 * kTileBytes];
+    __shared__ __attribute__((aligned(16))) char pe_tiles[3 * kPeTileBytes];
+    fwd_pcm_body<true, PAD>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe, tiles, pe_tiles);
+}
+
 // Persistent grid: one workgroup per compute unit (its LDS use admits one),
 // never more than there are items (token, 64-head group).
 static hipError_t persistent_blocks(int T, int H, unsigned* blocks) {
@@ -1023,16 +1122,23 @@ static hipError_t persistent_blocks(int T, int H, unsigned* blocks) {
     return hipSuccess;
 }
 
-hipError_t launch_fwd_pc(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
-                         int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
-                         hipStream_t s) {
+hipError_t launch_fwd(const uint16_t* q, const uint16_t* kv, const int32_t* idx, const float* sink,
+                      int T, int H, int N, int K, float scale, uint16_t* o, float* lse,
+                      hipStream_t s) {
+    if (T == 0) return hipSuccess;
     unsigned blocks = 0;
     const hipError_t e = persistent_blocks(T, H, &blocks);
     if (e != hipSuccess) return e;
-    if (H % 64 == 0)
+    if (K > kChunk) {
+        if (H % 64 == 0)
+            smla_k7_fwd_pcm<false><<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse);
+        else
+            smla_k7_fwd_pcm<true><<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse);
+    } else if (H % 64 == 0) {
         smla_k7_fwd_pc<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse);
-    else
+    } else {
         smla_k7_fwd_pcx<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse);
+    }
     return hipGetLastError();
 }
 
@@ -1055,16 +1161,23 @@ hipError_t launch_dq(const uint16_t* q, const uint16_t* kv, const uint16_t* dO, 
     return hipGetLastError();
 }
 
-hipError_t launch_fwd_pc_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
-                            const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
-                            uint16_t* o, float* lse, hipStream_t s) {
+hipError_t launch_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
+                         const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
+                         uint16_t* o, float* lse, hipStream_t s) {
+    if (T == 0) return hipSuccess;
     unsigned blocks = 0;
     const hipError_t e = persistent_blocks(T, H, &blocks);
     if (e != hipSuccess) return e;
-    if (H % 64 == 0)
+    if (K > kChunk) {
+        if (H % 64 == 0)
+            smla_k7_fwd_pcm_pe<false><<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe);
+        else
+            smla_k7_fwd_pcm_pe<true><<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe);
+    } else if (H % 64 == 0) {
         smla_k7_fwd_pc_pe<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe);
-    else
+    } else {
         smla_k7_fwd_pcx_pe<<<blocks, 512, 0, s>>>(q, kv, idx, sink, T, H, N, K, scale, o, lse, q_pe, k_pe);
+    }
     return hipGetLastError();
 }
 

@@ -39,14 +39,6 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own
-// L2).  Remap so that XCD x works on the x-th contiguous eighth of the
-// logical index range: neighbouring tokens then share an L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-    if ((nblocks & 7) != 0) return bid;
-    return (bid & 7) * (nblocks >> 3) + (bid >> 3);
-}
-
 __device__ __forceinline__ bool valid_row(int r, int num_kv) {
     return (unsigned)r < (unsigned)num_kv;
 }

@@ -742,6 +742,36 @@ def test_extreme_sink_values():
     assert_close("dkv", host_bf16(dkv), ref["dkv"])
 
 
+@pytest.mark.parametrize("H", [64, 48])
+def test_forward_chunks_with_empty_ones(H):
+    """Forward with topk 1600 (four index chunks, the last of 64 slots): a token
+    whose middle chunk is all masked, one whose trailing chunks are, one with a
+    single valid slot in its last chunk, an all-masked token, and random ones.
+    O and lse against the oracle; the all-masked token gets O = 0, lse = sink."""
+    T, N, K = 10, 900, 1600
+    rng = np.random.default_rng(1600 + H)
+    idx = rng.integers(0, N, size=(T, K)).astype(np.int32)
+    idx = np.where(rng.random((T, K)) < 0.3, -1, idx).astype(np.int32)
+    idx[0, 512:1024] = -1            # an empty middle chunk
+    idx[1, 1024:] = -1               # empty trailing chunks
+    idx[2, :] = -1
+    idx[2, K - 1] = 17               # one valid slot, in the last chunk
+    idx[3, :] = -1                   # no valid slot
+    idx[4, 1:] = -1                  # one valid slot, in the first chunk
+    x = {"q": inputs.normal_bf16((T, H, 512), 1600 + H, 1), "kv": inputs.normal_bf16((N, 512), 1600 + H, 2),
+         "idx": idx, "sink": rng.standard_normal(H).astype(np.float32)}
+    _say(f"[fwd chunks] H={H} K={K}")
+    O64, lse64 = orc.forward(x["q"], x["kv"], x["idx"], x["sink"], SCALE)
+    o, lse = B.smla_fwd(dev_bf16(x["q"]), dev_bf16(x["kv"]), dev(x["idx"]), dev(x["sink"]), SCALE)
+    torch.cuda.synchronize()
+    got_o = host_bf16(o)
+    got_l = lse.cpu().numpy().astype(np.float64)
+    assert_close("O", got_o, O64)
+    assert np.max(np.abs(got_l - lse64)) < 1e-4
+    assert np.all(got_o[3] == 0.0)
+    np.testing.assert_allclose(got_l[3], x["sink"].astype(np.float64), rtol=1e-6, atol=1e-6)
+
+
 def _fuzz_case(seed):
     """A random small problem: any H the library takes, topk up to two index chunks,
     slots drawn with replacement (duplicate rows within a token), -1 padding and a
