@@ -38,13 +38,16 @@ constexpr int kOBytes = kBK * kOPitch;                  // one tile of output ro
 
 // NKS = 2H / 32 reduction steps (H = 16 * NKS).
 //
-// PE (the has_pe=True variant, H a multiple of 32) also forms the positional
-// intermediate interm_pe [T*topk, 64] = sum_h scale*dS . q_pe (bf16), from the
-// same dS fragments: q_pe_t is staged in LDS (rows 160 bytes apart) and each
+// PE (the has_pe=True variant) also forms the positional intermediate
+// interm_pe [T*topk, 64] = sum_h scale*dS . q_pe (bf16), from the same dS
+// fragments: q_pe_t is staged in LDS (rows 160 bytes apart) and each
 // MFMA-first wave 4 + e holds the transposed fragments of positional columns
-// 16e .. 16e+15 over the H dS rows (the first H/32 reduction steps), adds one
-// MFMA per such step, and stores its 16 columns of the tile's rows from a
-// small LDS tile at the next tile, whole 128-byte rows, one store per wave.
+// 16e .. 16e+15 over the H dS rows (the first ceil(H/32) reduction steps),
+// adds one MFMA per such step, and stores its 16 columns of the tile's rows
+// from a small LDS tile at the next tile, whole 128-byte rows, one store per
+// wave.  With H an odd multiple of 16 the last of these steps also spans the
+// first 16 P rows; the upper half of its q_pe fragment is zero, so they add
+// nothing.
 template <int NKS, bool PE>
 __global__ __attribute__((amdgpu_flat_work_group_size(kIThreads, kIThreads), amdgpu_waves_per_eu(2, 2)))
 void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__ dO,
@@ -55,8 +58,7 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     constexpr int R = 2 * H;
     constexpr int kYBytes = R * kYPitch;                 // one dsp block in LDS (padded rows)
     constexpr int kYChunks = R * kBK * 2 / 16;           // 16-B chunks of one dsp block
-    static_assert(!PE || NKS % 2 == 0, "the positional part needs H % 32 == 0");
-    constexpr int NKP = NKS / 2;                         // reduction steps over the dS rows
+    constexpr int NKP = (NKS + 1) / 2;                   // reduction steps over the dS rows
     constexpr int kPeOPitch = kPeRow + 16;               // positional output row in LDS
     constexpr int kPeOBytes = kBK * kPeOPitch;
     static_assert(kYRing * kYBytes + 2 * kOBytes + (PE ? 2 * kPeOBytes : 0) <= 2 * kStageBytes,
@@ -143,7 +145,7 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         if (p + 2 < kPasses) issue_pass(p + 2);
     }
     // xfp[ks] (waves 4-7, e = w - 4): positional column 16e + c16 of q_pe rows
-    // 32ks + 4g .. +3, then 32ks + 16 + 4g .. +3
+    // 32ks + 4g .. +3, then 32ks + 16 + 4g .. +3 (zeros for rows past H)
     u32x4 xfp[PE ? NKP : 1];
     if constexpr (PE) {
 #pragma unroll
@@ -157,7 +159,8 @@ void smla_k3_interm(const uint16_t* __restrict__ q, const uint16_t* __restrict__
 #pragma unroll
             for (int ks = 0; ks < NKP; ++ks) {
                 const u32x2 lo = ds_read_tr16(xpe + xpb + 32 * ks * kXpPitch);
-                const u32x2 hi = ds_read_tr16(xpe + xpb + (32 * ks + 16) * kXpPitch);
+                const u32x2 hi = 32 * ks + 16 < H ? ds_read_tr16(xpe + xpb + (32 * ks + 16) * kXpPitch)
+                                                  : u32x2{0u, 0u};
                 xfp[ks] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
         }
@@ -340,9 +343,13 @@ hipError_t launch_interm_fused_pe(const uint16_t* q, const uint16_t* dO, const u
         smla_k3_interm<nks, true><<<T, kIThreads, 0, s>>>(q, dO, dsp, idx, N, K, interm, q_pe, interm_pe); \
         break;
     switch (H / 16) {
+        SMLA_INTERM_PE_CASE(1)
         SMLA_INTERM_PE_CASE(2)
+        SMLA_INTERM_PE_CASE(3)
         SMLA_INTERM_PE_CASE(4)
+        SMLA_INTERM_PE_CASE(5)
         SMLA_INTERM_PE_CASE(6)
+        SMLA_INTERM_PE_CASE(7)
         SMLA_INTERM_PE_CASE(8)
         default: return hipErrorInvalidValue;
     }

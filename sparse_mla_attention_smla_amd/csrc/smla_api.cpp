@@ -909,15 +909,9 @@ int smla_bwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, con
     if (launch_dq_pe(q, q_pe, kv, k_pe, dO, lse, delta, idx, T, H, num_kv, topk, scale, dq, dq_pe, dsp, s) !=
         hipSuccess)
         return SMLA_ERR_HIP;
-    if (H % 32 == 0) {
-        // one pass over the dS/P blocks forms both intermediates
-        if (launch_interm_fused_pe(q, dO, q_pe, dsp, idx, T, H, num_kv, topk, interm, interm_pe, s) != hipSuccess)
-            return SMLA_ERR_HIP;
-    } else {
-        if (launch_interm(q, dO, dsp, idx, T, H, num_kv, topk, interm, s) != hipSuccess) return SMLA_ERR_HIP;
-        if (launch_interm_pe(q_pe, dsp, idx, T, H, num_kv, topk, interm_pe, s) != hipSuccess)
-            return SMLA_ERR_HIP;
-    }
+    // one pass over the dS/P blocks forms both intermediates
+    if (launch_interm_fused_pe(q, dO, q_pe, dsp, idx, T, H, num_kv, topk, interm, interm_pe, s) != hipSuccess)
+        return SMLA_ERR_HIP;
     if (side != nullptr && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SMLA_ERR_HIP;
     if (launch_gather_sum(interm, row_ptr, slots, M, num_kv, gs, dkv, s) != hipSuccess) return SMLA_ERR_HIP;
     if (launch_gather_pe(interm_pe, row_ptr, slots, M, num_kv, gs, pe_partial, dk_pe, s) != hipSuccess)

@@ -80,9 +80,7 @@ hipError_t launch_dq_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t*
 hipError_t launch_fwd_pe(const uint16_t* q, const uint16_t* q_pe, const uint16_t* kv, const uint16_t* k_pe,
                          const int32_t* idx, const float* sink, int T, int H, int N, int K, float scale,
                          uint16_t* o, float* lse, hipStream_t s);
-hipError_t launch_interm_pe(const uint16_t* q_pe, const uint16_t* dsp, const int32_t* idx, int T, int H,
-                            int N, int K, uint16_t* interm_pe, hipStream_t s);
-// both intermediates of the has_pe=True variant in one pass (H % 32 == 0)
+// both intermediates of the has_pe=True variant in one pass
 hipError_t launch_interm_fused_pe(const uint16_t* q, const uint16_t* dO, const uint16_t* q_pe,
                                   const uint16_t* dsp, const int32_t* idx, int T, int H, int N, int K,
                                   uint16_t* interm, uint16_t* interm_pe, hipStream_t s);

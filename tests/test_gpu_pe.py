@@ -244,11 +244,13 @@ def test_pe_autograd_function():
     assert_close("autograd d_sink", sink.grad.cpu().numpy(), ref["d_sink"])
 
 
-@pytest.mark.parametrize("H", [32, 48])
+@pytest.mark.parametrize("H", [16, 32, 48, 80])
 def test_pe_full_rows_other_head_counts(H):
-    """has_pe=True at 32 heads (slot-split producers) and 48 (a padded last
-    group), 700 tokens, so persistent workgroups stream across items: every row
-    of dq, dq_pe, dkv, dk_pe and d_sink, and the forward's O and lse."""
+    """has_pe=True at 16 and 32 heads (slot-split producers), 48 and 80 (a padded
+    last group; with 16 and 48 the intermediate's last positional step is half
+    dS rows, half zeros), 700 tokens, so persistent workgroups stream across
+    items: every row of dq, dq_pe, dkv, dk_pe and d_sink, and the forward's O
+    and lse."""
     w = inputs.Workload(f"pe_h{H}", 60 + H // 16, T=700, H=H, num_kv=875, topk=512, selection="swa_pool",
                         window=128, pool_stride=4, pool_picks=384)
     x = dict(inputs.make(w, sink=True))
