@@ -322,14 +322,32 @@ def cpu_baseline(w, n_tokens):
         orc.backward(q, x["kv"], dO, Os, ls, ix, x["sink"], scale)
         dt += time.perf_counter() - t0
     flops = 10.0 * n_tokens * w.H * w.topk * D
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    pools = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in pools] or [1])
+    blas = ", ".join(sorted({f"{i.get('internal_api', '?')} {i.get('version', '?')} "
+                             f"({i.get('threading_layer', '?')}, {i.get('num_threads', '?')} threads)"
+                             for i in pools if i.get("user_api") == "blas"})) or "unknown"
     return {
         "value": flops / dt / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
         "sample": f"fp64 NumPy oracle backward (delta, dq, P, dS, interm, dkv accumulation, d_sink) "
                   f"on {n_tokens} evenly spaced of {w.T} tokens of the {w.name} workload; "
                   f"{dt:.2f} s; extrapolated {dt * w.T / n_tokens * 1e3:.0f} ms per full call",
         "host_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": _cpu_model(),
+        "blas": blas,
     }
+
+
+def _cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (unknown elsewhere)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():

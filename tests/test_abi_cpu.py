@@ -206,6 +206,19 @@ def test_traffic_hash_ignores_comments_only():
     assert len(bench.kernel_source_hash()) == 16
 
 
+def test_cpu_baseline_record_on_a_small_sample():
+    # the bench's CPU leg: the oracle backward timed on a token sample, with the
+    # host it ran on (threads, CPU model, BLAS) recorded beside the rate
+    import bench
+    from sparse_mla_attention_smla_amd import inputs
+    rec = bench.cpu_baseline(inputs.WORKLOADS["tiny"], 8)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOPS" and rec["value"] > 0
+    assert rec["cores"] >= 1 and rec["host_cpus"] >= 1
+    assert isinstance(rec["cpu_model"], str) and rec["cpu_model"]
+    assert isinstance(rec["blas"], str) and rec["blas"]
+    assert "8 evenly spaced of 64 tokens" in rec["sample"]
+
+
 def test_dsp_piece_layout_helpers_match_the_documented_offsets():
     """The test helpers that read and build dS/P blocks follow the offset formula
     documented with smla_dq in include/smla.h (host-side index bookkeeping)."""
