@@ -500,7 +500,7 @@ def test_forward_matches_oracle(name, sink):
     (19, 32, 19, 16, True),     # 32 heads: a padded group of two 16-head blocks
     (21, 96, 45, 64, False),    # 96 heads: a full group and a padded one, no sink
     (25, 48, 33, 40, True),     # 48 heads: a padded group of three blocks
-    (12, 64, 80, 600, True),    # topk beyond one index chunk: the one-wave-per-16-heads kernel
+    (12, 64, 80, 600, True),    # topk beyond one index chunk: the multi-segment persistent forward
 ])
 def test_forward_ragged(T, H, N, K, sink):
     x = _custom(T, H, N, K, seed=7 * T + H, sink=sink, pool_frac=0.5)
