@@ -269,6 +269,26 @@ def test_pe_full_rows_other_head_counts(H):
     assert np.max(np.abs(lse.cpu().numpy().astype(np.float64)[fin] - x["lse"][fin].astype(np.float64))) < 1e-4
 
 
+def test_pe_full_rows_past_4gib_of_intermediate():
+    """has_pe=True on 16384 tokens of 16 heads: the intermediate holds 8 GiB, so
+    the later tokens' intermediate rows, dS/P blocks and slot ids sit past 2^32
+    bytes (as in the plain test of that shape), and the positional intermediate
+    (1 GiB), dq_pe and the positional gather address those tokens too: every row
+    of dq, dq_pe, dkv, dk_pe and d_sink against the oracle."""
+    w = inputs.Workload("pe_t16384_h16", 70, T=16384, H=16, num_kv=20480, topk=512, selection="swa_pool",
+                        window=128, pool_stride=4, pool_picks=384)
+    x = dict(inputs.make(w, sink=True))
+    x["q_pe"], x["k_pe"] = inputs.make_pe(w)
+    x["scale"] = SCALE_PE
+    x = _with_forward(x)
+    _say(f"[pe rows] T={w.T} H={w.H}")
+    got = _bwd(_dev(x), x)
+    _say(f"[pe rows] T={w.T}: oracle backward over all tokens")
+    ref = oracle_backward_chunked(x)
+    _check(f"T={w.T} H={w.H}", x, ref, got)
+    torch.cuda.empty_cache()
+
+
 def test_pe_zero_positional_parts_equal_the_plain_backward():
     """q_pe = 0: every logit is the plain one, so smla_bwd_pe must give smla_bwd's
     dq, dkv and d_sink (the plain call may take another dQ kernel, so up to
