@@ -882,6 +882,47 @@ def test_topk_beyond_one_chunk(H, sink):
     assert_close("dkv (phased)", host_bf16(dkv2), ref["dkv"])
 
 
+def _many_multi_segment_items(T, H, N, K, seed):
+    """T tokens whose topk spans several 512-slot index chunks: the even tokens'
+    slots shuffled (valid ones in every chunk), one all-masked token, one whose
+    valid slots lie only in its last chunk, one with a single valid slot."""
+    x = _custom(T, H, N, K, seed=seed, sink=True, pool_frac=1.0)
+    x["idx"][::2] = inputs.shuffle_slots(x["idx"][::2], seed=seed)
+    x["idx"][7] = -1
+    x["idx"][8, : (K - 1) // 512 * 512] = -1
+    x["idx"][9, 1:] = -1
+    return x
+
+
+@pytest.mark.parametrize("H", [128, 48])
+def test_topk_beyond_one_chunk_many_items(H):
+    """topk 1100 on 600 tokens: each persistent workgroup takes several items of
+    three segments each, so the dQ stream reloads q/dO and the forward's
+    consumers finish a head from the published softmax state while the next
+    item's first tiles are already produced (48 heads: with a padded group).
+    Every dq, dkv, O and lse row against the oracle; the all-masked token exact."""
+    T, N, K = 600, 900, 1100
+    x = _with_forward(_many_multi_segment_items(T, H, N, K, seed=5 * K + H))
+    _say(f"[topk>512 many] T={T} H={H} N={N} K={K}: valid per row min "
+         f"{int(np.sum(x['idx'] >= 0, axis=1).min())} max {int(np.sum(x['idx'] >= 0, axis=1).max())}")
+    d = _to_dev(x)
+    o, lse = B.smla_fwd(d["q"], d["kv"], d["idx"], d["sink"], SCALE)
+    dq, dkv, ds = _run_bwd(d)
+    r, _, worst = assert_close("O", host_bf16(o), x["O64"])
+    _say(f"[topk>512 many] H={H}: O rel-L2 {r:.2e} worst row {worst:.2e}")
+    got_l = lse.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(got_l - x["lse"].astype(np.float64))) < 1e-4
+    assert np.all(host_bf16(o)[7] == 0.0)
+    ref = oracle_backward_chunked(x, chunk=16)
+    for name, g in (("dq", dq), ("dkv", dkv)):
+        r, _, worst = assert_close(name, host_bf16(g), ref[name])
+        _say(f"[topk>512 many] H={H}: {name} rel-L2 {r:.2e} worst row {worst:.2e}")
+    assert np.all(host_bf16(dq)[7] == 0.0)
+    assert_close("d_sink", ds.cpu().numpy(), ref["d_sink"])
+    del d
+    torch.cuda.empty_cache()
+
+
 def test_shuffled_slots_invalid_indices_and_padding():
     x = dict(workload("small"))
     idx = inputs.shuffle_slots(x["idx"], seed=5)

@@ -269,6 +269,32 @@ def test_pe_full_rows_other_head_counts(H):
     assert np.max(np.abs(lse.cpu().numpy().astype(np.float64)[fin] - x["lse"][fin].astype(np.float64))) < 1e-4
 
 
+@pytest.mark.parametrize("H", [128, 48])
+def test_pe_topk_beyond_one_chunk_many_items(H):
+    """has_pe=True with topk 1100 on 600 tokens (duplicates, -1 and out-of-range
+    slots in every index chunk): each persistent workgroup takes several items
+    of three segments, in the dQ stream and in the multi-chunk forward (48
+    heads: a padded group).  Every row of O, lse, dq, dq_pe, dkv, dk_pe and
+    d_sink against the oracle."""
+    T, N, K = 600, 900, 1100
+    x = _custom_pe(T, H, N, K, seed=11 * H, sink=True, dup=True)
+    _say(f"[pe topk>512 many] T={T} H={H} N={N} K={K}")
+    d = _dev(x)
+    o, lse = B.smla_fwd_pe(d["q"], d["q_pe"], d["kv"], d["k_pe"], d["idx"], d["sink"], x["scale"])
+    torch.cuda.synchronize()
+    r, _, worst = assert_close("O (pe topk>512)", host_bf16(o), x["O64"])
+    _say(f"[pe topk>512 many] H={H}: O rel-L2 {r:.2e} worst row {worst:.2e}")
+    got_l = lse.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(x["lse"])
+    assert np.array_equal(np.isfinite(got_l), fin)
+    assert np.max(np.abs(got_l[fin] - x["lse"][fin].astype(np.float64)), initial=0.0) < 1e-4
+    got = _bwd(d, x)
+    ref = oracle_backward_chunked(x, chunk=16)
+    _check(f"topk>512 T={T} H={H}", x, ref, got)
+    del d
+    torch.cuda.empty_cache()
+
+
 def test_pe_full_rows_past_4gib_of_intermediate():
     """has_pe=True on 16384 tokens of 16 heads: the intermediate holds 8 GiB, so
     the later tokens' intermediate rows, dS/P blocks and slot ids sit past 2^32
