@@ -894,12 +894,13 @@ def _many_multi_segment_items(T, H, N, K, seed):
     return x
 
 
-@pytest.mark.parametrize("H", [128, 48])
+@pytest.mark.parametrize("H", [128, 48, 16])
 def test_topk_beyond_one_chunk_many_items(H):
     """topk 1100 on 600 tokens: each persistent workgroup takes several items of
     three segments each, so the dQ stream reloads q/dO and the forward's
     consumers finish a head from the published softmax state while the next
-    item's first tiles are already produced (48 heads: with a padded group).
+    item's first tiles are already produced (48 heads: with a padded group; 16:
+    the slot-split dQ and a padded forward).
     Every dq, dkv, O and lse row against the oracle; the all-masked token exact."""
     T, N, K = 600, 900, 1100
     x = _with_forward(_many_multi_segment_items(T, H, N, K, seed=5 * K + H))

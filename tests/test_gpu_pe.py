@@ -269,12 +269,12 @@ def test_pe_full_rows_other_head_counts(H):
     assert np.max(np.abs(lse.cpu().numpy().astype(np.float64)[fin] - x["lse"][fin].astype(np.float64))) < 1e-4
 
 
-@pytest.mark.parametrize("H", [128, 48])
+@pytest.mark.parametrize("H", [128, 48, 32])
 def test_pe_topk_beyond_one_chunk_many_items(H):
     """has_pe=True with topk 1100 on 600 tokens (duplicates, -1 and out-of-range
     slots in every index chunk): each persistent workgroup takes several items
     of three segments, in the dQ stream and in the multi-chunk forward (48
-    heads: a padded group).  Every row of O, lse, dq, dq_pe, dkv, dk_pe and
+    heads: a padded group; 32: the slot-split dQ).  Every row of O, lse, dq, dq_pe, dkv, dk_pe and
     d_sink against the oracle."""
     T, N, K = 600, 900, 1100
     x = _custom_pe(T, H, N, K, seed=11 * H, sink=True, dup=True)
